@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused reduce + residual-add + RMSNorm step on one MI355X.
+
+A step is one pass of the hot path over one batch of the workload: the host
+split plan for the batch (integer arithmetic, microseconds) and the fused
+kernel launch(es) it calls for.  At the default workload (Llama-3-70B-shaped:
+T=1024 tokens, h=8192, N=8 bf16 partials) the planner keeps the batch whole
+(its GEMM is one wave on 256 CUs), so a step is one fused launch.
+
+Timing: W untimed warm-up steps, then K timed steps back to back on the
+current torch stream -- the stream the library enqueues on -- between two HIP
+events, with torch.cuda.synchronize() on both sides.  Input sets rotate so
+that the bytes touched between two uses of one set exceed twice the 256 MB
+last-level (MALL) cache: every read is served by HBM, not by that cache.
+
+Printed: one JSON line.  `value` is algorithmic GB/s, (N+1 reads + 2 writes)
+x T x h x sizeof(bf16) per step over the measured time per step; `roofline`
+prices the same bytes against the 8 TB/s HBM peak; `cpu_baseline` times the
+float64 CPU oracle on a bounded sample of the same workload on one host core.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, decimal GB/s
+MALL_BYTES = 256 * 1000 * 1000  # MI355X Infinity Cache (last-level, memory side)
+KERNEL_SOURCE = os.path.join(ROOT, "reduce_rmsnorm_amd", "csrc", "fused_reduce_rmsnorm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_reduce_rmsnorm_llama70b_traffic.json")
+METRIC = "fused reduce-add-RMSNorm HBM GB/s (% of peak), h=8192 T=1024 N=8 bf16"
+
+# GEMM tile model for the split planner: 256x256 output tiles, one CTA per CU.
+GEMM_TILE = 256
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="llama70b")
+    ap.add_argument("--mode", choices=("full", "shard"), default="full",
+                    help="full: every row; shard: shard 0's rows (one rank's share)")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input sets to rotate through (0: enough to exceed 2x the MALL)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="budget of the CPU oracle sample (0 disables the cpu_baseline leg)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, d, budget_s: float) -> dict:
+    """Time the float64 oracle as it stands on whole rows of the same batch,
+    pinned to one host core, until the budget is spent or all rows are done."""
+    import numpy as np  # noqa: F401
+    import oracle
+    parts = list(d["partials"])
+    T = wl.num_tokens
+    try:
+        saved = os.sched_getaffinity(0)
+        core = min(saved)
+        os.sched_setaffinity(0, {core})
+    except (AttributeError, OSError):
+        saved = None
+    try:
+        rows_done = 0
+        t0 = time.perf_counter()
+        chunk = 8
+        while rows_done < T and time.perf_counter() - t0 < budget_s:
+            rows = range(rows_done, min(T, rows_done + chunk))
+            oracle.fused_reduce_rmsnorm(parts, d["residual"], d["weight"], d["eps"], wl.dtype,
+                                        rows=rows)
+            rows_done = rows.stop
+        elapsed = time.perf_counter() - t0
+    finally:
+        if saved is not None:
+            os.sched_setaffinity(0, saved)
+    gbs = wl.algorithmic_bytes(rows_done) / elapsed / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows_done} of {T} rows of the same {wl.name} batch, float64 NumPy "
+                      f"oracle, one pass, {elapsed:.1f} s on 1 pinned core of "
+                      f"{len(saved) if saved else os.cpu_count()}",
+            "tokens_per_s": round(rows_done / elapsed, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import reduce_rmsnorm_amd as tw
+    from synthetic import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    tw.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = WORKLOADS[args.workload]
+    T, h, N = wl.num_tokens, wl.hidden, wl.num_partials
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+    d = make_inputs(wl)
+
+    def up(a):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    if args.mode == "shard":
+        lo, hi = (0 * T) // N, (1 * T) // N
+    else:
+        lo, hi = 0, T
+    rows = hi - lo
+    step_bytes = wl.algorithmic_bytes(rows)
+    R = args.rotate or max(1, math.ceil(2 * MALL_BYTES / step_bytes) + 1)
+
+    base_parts, base_res, w = up(d["partials"]), up(d["residual"]), up(d["weight"])
+    sets = []
+    for r in range(R):
+        parts = base_parts if r == 0 else base_parts.clone()
+        res = base_res if r == 0 else base_res.clone()
+        sets.append((parts, res, torch.empty_like(res), torch.empty_like(res)))
+    stream = torch.cuda.current_stream(dev)
+
+    plan_kw = dict(tokens_per_cta=GEMM_TILE, ctas_per_token_tile=max(1, h // GEMM_TILE),
+                   num_cus=256, ctas_per_cu=1,
+                   min_split_tokens=4096 if wl.name == "mixtral" else 1024)
+
+    def step(i):
+        parts, res, out, rout = sets[i % R]
+        if args.mode == "shard":
+            tw.tw_shard_rmsnorm(parts, res, w, wl.eps, 0, out=out, residual_out=rout, stream=stream)
+            return 1
+        plan = tw.tw_split_plan(T, **plan_kw)
+        if plan["reason"] == 0:
+            tw.tw_fused_reduce_rmsnorm_split(parts, res, w, wl.eps, plan["prefix_tokens"],
+                                             out=out, residual_out=rout, stream=stream)
+            return 2
+        tw.tw_fused_reduce_rmsnorm(parts, res, w, wl.eps, out=out, residual_out=rout, stream=stream)
+        return 1
+
+    print(f"[bench] workload={wl.name} mode={args.mode} rows={rows} h={h} N={N} {wl.dtype} "
+          f"rotate={R} warmup={args.warmup} steps={args.steps}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    launches = 0
+    start.record(stream)
+    for i in range(args.steps):
+        launches += step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    ms_per_step = ms / args.steps
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms, {ms_per_step * 1e3:.2f} us/step, "
+          f"{gbs:.1f} GB/s", file=sys.stderr, flush=True)
+
+    if args.copy_probe:
+        n = 512 * 1024 * 1024
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: 5 x {n} bytes device-to-device", file=sys.stderr, flush=True)
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE) and args.mode == "full" and wl.name == "llama70b":
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha256") == kernel_source_hash():
+            traffic = tr.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: T={T} h={h} N={N} bf16 storage, "
+                               f"{args.mode} mode ({rows} rows), eps={wl.eps}",
+                   "num_tokens": T, "hidden": h, "num_partials": N, "storage_dtype": wl.dtype,
+                   "mode": args.mode, "rows": rows, "rotated_input_sets": R,
+                   "launches_per_step": launches / args.steps},
+        "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(rows / (ms_per_step * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": step_bytes * args.steps // max(1, launches),
+                     "avg_launch_us": round(ms * 1e3 / max(1, launches), 3)},
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, d, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

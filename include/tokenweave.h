@@ -1,0 +1,186 @@
+/*
+ * tokenweave.h -- C ABI of the MI355X (gfx950) fused reduce + residual-add +
+ * RMSNorm library and its wave-aware split planner.
+ *
+ * Sources, by page title and section:
+ *   [Blog]  "TokenWeave: Why Hiding Tensor-Parallel Communication Needs Wave
+ *           Arithmetic, Not Finer Tiles" -- sections "The overlap trap",
+ *           "Fix one: split at wave boundaries, unequally" and "Fix two:
+ *           RMSNorm was never insignificant" (the per-CTA kernel sketch).
+ *   [Guide] "TokenWeave Guide: Compute-Communication Overlap for LLMs" --
+ *           section "Fused AllReduce-RMSNorm: Bypassing Global Memory" (the
+ *           RMSNorm equation).
+ *
+ * The header uses only C types: streams are opaque `void*` (a hipStream_t,
+ * NULL for the null stream), so it can be included without HIP headers and
+ * loaded with ctypes.
+ *
+ * Ownership and threading
+ *   - The caller owns all memory.  The library never allocates, frees or
+ *     synchronizes device memory; kernels are enqueued on the caller's stream
+ *     and the call returns after the enqueue.
+ *   - Device faults surface at the caller's next synchronization; launch
+ *     errors come back as TW_ERR_DEVICE.
+ *   - The only global state is a thread-local last-error string, so calls
+ *     from several host threads are safe.
+ *
+ * Errors: every argument is checked before any HIP call is made, so an
+ * argument error never touches the device.
+ */
+#ifndef TOKENWEAVE_H_
+#define TOKENWEAVE_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TW_OK = 0,
+  TW_ERR_INVALID_ARG = 1,   /* argument out of its documented range */
+  TW_ERR_UNSUPPORTED = 2,   /* valid, but outside what the kernels handle */
+  TW_ERR_DEVICE = 3         /* the HIP runtime reported an error */
+} tw_status;
+
+typedef enum {
+  TW_F32 = 0,               /* IEEE binary32 */
+  TW_BF16 = 1               /* bfloat16: the upper 16 bits of a binary32 */
+} tw_dtype;
+
+#define TW_MAX_PARTIALS 16        /* tensor-parallel degree N handled */
+#define TW_MAX_ROW_BYTES 131072   /* largest hidden * sizeof(dtype): h <= 65536
+                                     for bf16, h <= 32768 for fp32 */
+#define TW_MAX_TOKENS 2147483647  /* largest num_tokens (one workgroup per row) */
+
+#define TW_ABI_VERSION 1
+
+/* Version of this ABI (TW_ABI_VERSION of the built library). */
+int32_t tw_abi_version(void);
+
+/*
+ * tw_fused_reduce_rmsnorm -- the fused step for every token row.
+ *
+ * [Blog] "Fix two", kernel sketch, and [Guide] RMSNorm equation.  For each
+ * row t < num_tokens, in float32 arithmetic:
+ *     x      = sum_{i<N} partials[i][t,:] + residual[t,:]
+ *     rs     = 1 / sqrt( (sum_j x_j^2) / hidden + eps )
+ *     out[t,:]          = round_dtype( (x * rs) * weight )
+ *     residual_out[t,:] = round_dtype( x )
+ * The N partials stand for the row-parallel GEMM outputs of N tensor-parallel
+ * ranks (on the pages the NVSwitch reduces them; here they are N buffers in
+ * this GPU's memory).  The partial sum is a compensated (error-free
+ * transformation) float32 sum; rounding to bf16 is round-to-nearest-even.
+ *
+ * Arguments
+ *   partials      host array of num_partials device pointers, each to a
+ *                 row-major [num_tokens, hidden] tensor of `dtype`
+ *   num_partials  N, 1..TW_MAX_PARTIALS
+ *   residual      device [num_tokens, hidden] `dtype`
+ *   weight        device [hidden] `dtype` (the RMSNorm gamma)
+ *   out           device [num_tokens, hidden] `dtype`, written
+ *   residual_out  device [num_tokens, hidden] `dtype`, written; may equal
+ *                 `residual` exactly (in-place update)
+ *   num_tokens    T >= 0; T == 0 is a no-op returning TW_OK
+ *   hidden        h >= 1; must be a multiple of 16/sizeof(dtype), with
+ *                 h * sizeof(dtype) <= TW_MAX_ROW_BYTES
+ *   eps           finite, >= 0, added to the mean of squares under the root
+ *   dtype         element type of every tensor
+ *   stream        hipStream_t to enqueue on, NULL for the null stream
+ *
+ * Errors
+ *   TW_ERR_INVALID_ARG  N out of range, T < 0, h < 1, eps negative or not
+ *                       finite, a NULL pointer when T > 0, an output range
+ *                       overlapping an input or the other output (except
+ *                       residual_out == residual), an unknown dtype value
+ *   TW_ERR_UNSUPPORTED  a pointer not 16-byte aligned, h not a multiple of
+ *                       16/sizeof(dtype), h * sizeof(dtype) > TW_MAX_ROW_BYTES,
+ *                       num_tokens > TW_MAX_TOKENS
+ *   TW_ERR_DEVICE       the launch failed (see tw_last_error())
+ */
+tw_status tw_fused_reduce_rmsnorm(const void* const* partials, int32_t num_partials,
+                                  const void* residual, const void* weight,
+                                  void* out, void* residual_out,
+                                  int64_t num_tokens, int64_t hidden, float eps,
+                                  tw_dtype dtype, void* stream);
+
+/*
+ * tw_shard_rmsnorm -- the fused step on one rank's token shard.
+ *
+ * [Blog] "Fix two": after a ReduceScatter split at token boundaries each of
+ * the N ranks owns complete rows for 1/N of the tokens and normalizes only
+ * those.  Shard k covers rows [floor(k*T/N), floor((k+1)*T/N)) with N =
+ * num_partials.  Every tensor argument is the FULL [num_tokens, hidden]
+ * buffer; only the shard's rows are read (of partials and residual) and
+ * written (of out and residual_out), at their own row offsets, and all other
+ * rows are left untouched.  Per-row arithmetic is bit-identical to
+ * tw_fused_reduce_rmsnorm.
+ *
+ * Arguments are those of tw_fused_reduce_rmsnorm plus
+ *   shard_index   k, 0 <= k < num_partials (else TW_ERR_INVALID_ARG)
+ * An empty shard (T < N) is a no-op returning TW_OK.
+ */
+tw_status tw_shard_rmsnorm(const void* const* partials, int32_t num_partials,
+                           const void* residual, const void* weight,
+                           void* out, void* residual_out,
+                           int64_t num_tokens, int64_t hidden, float eps,
+                           tw_dtype dtype, int32_t shard_index, void* stream);
+
+/*
+ * Split planner: [Blog] "The overlap trap" and "Fix one".  A GEMM over M
+ * token rows launches ceil(M / tokens_per_cta) * ctas_per_token_tile CTAs;
+ * a wave holds num_cus * ctas_per_cu of them; waves(M) = ceil(CTAs / that).
+ * The batch of T tokens is split in two, prefix = floor(T/2) + offset and
+ * suffix = T - prefix, with the first offset (in the given order) below
+ * floor(T/2) for which waves(prefix) + waves(suffix) <= waves(T).  No split
+ * when T == 0, when T < min_split_tokens, when waves(T) <= 1, or when no
+ * offset qualifies; then prefix = T, suffix = 0, offset = -1.
+ */
+typedef struct {
+  int64_t num_tokens;           /* T = B * L, >= 0 */
+  int64_t tokens_per_cta;       /* GEMM tile rows (M-tile), >= 1 */
+  int64_t ctas_per_token_tile;  /* GEMM tiles across the output features, >= 1 */
+  int32_t num_cus;              /* compute units (256 on MI355X), >= 1 */
+  int32_t ctas_per_cu;          /* resident CTAs per CU in one wave, >= 1 */
+  int64_t min_split_tokens;     /* split threshold, >= 0 (0 disables it) */
+  const int32_t* offsets;       /* candidate offsets, strictly ascending,
+                                   >= 0; NULL selects {0,64,128,192,256,512} */
+  int32_t num_offsets;          /* length of offsets (0 when offsets is NULL) */
+} tw_split_problem;
+
+#define TW_PLAN_SPLIT 0
+#define TW_PLAN_BELOW_THRESHOLD 1
+#define TW_PLAN_SINGLE_WAVE 2
+#define TW_PLAN_NO_FEASIBLE_OFFSET 3
+#define TW_PLAN_EMPTY 4
+
+typedef struct {
+  int64_t prefix_tokens;
+  int64_t suffix_tokens;
+  int32_t offset;               /* -1 when not split */
+  int32_t waves_unsplit;
+  int32_t waves_prefix;
+  int32_t waves_suffix;
+  int32_t reason;               /* one of TW_PLAN_* */
+} tw_split_plan_result;
+
+/*
+ * tw_split_plan -- host only, integer arithmetic, no device call.
+ *   in, out       non-NULL (else TW_ERR_INVALID_ARG)
+ * Errors: TW_ERR_INVALID_ARG for a field out of range or offsets not
+ * strictly ascending; TW_ERR_UNSUPPORTED when num_tokens exceeds 2^40,
+ * ctas_per_token_tile exceeds 2^20 or a wave count does not fit in int32.
+ */
+tw_status tw_split_plan(const tw_split_problem* in, tw_split_plan_result* out);
+
+/* Static description of a status code. */
+const char* tw_status_string(tw_status s);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* tw_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOKENWEAVE_H_ */

@@ -1,0 +1,22 @@
+"""MI355X (gfx950) fused reduce + residual-add + RMSNorm with a wave-aware
+token-split planner, behind the C ABI in ``include/tokenweave.h``.
+
+The Python names mirror the C entry points:
+
+* :func:`tw_fused_reduce_rmsnorm` -- every row,
+* :func:`tw_shard_rmsnorm` -- one rank's token shard,
+* :func:`tw_split_plan` -- the prefix/suffix split plan,
+* :func:`tw_fused_reduce_rmsnorm_split` -- the two launches of a split.
+"""
+
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    PLAN_REASONS,
+    TokenWeaveError,
+    declared_functions,
+    load_library,
+    tw_fused_reduce_rmsnorm,
+    tw_fused_reduce_rmsnorm_split,
+    tw_shard_rmsnorm,
+    tw_split_plan,
+)

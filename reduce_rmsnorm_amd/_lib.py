@@ -1,0 +1,219 @@
+"""ctypes binding of ``libtokenweave.so`` (argument marshalling only).
+
+Every step of the fused path runs in the library's HIP kernels; this module
+only turns torch tensors into device pointers and the current torch stream
+into a ``hipStream_t``, and turns status codes into exceptions.  torch is
+imported before the library is loaded so that both share the one HIP runtime
+already in the process.
+
+There is no CPU fallback: if the library is not built, or a tensor is not on
+a GPU, the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence, Union
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtokenweave.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tokenweave.h")
+
+TW_OK, TW_ERR_INVALID_ARG, TW_ERR_UNSUPPORTED, TW_ERR_DEVICE = 0, 1, 2, 3
+TW_F32, TW_BF16 = 0, 1
+TW_MAX_PARTIALS = 16
+
+PLAN_REASONS = {0: "split", 1: "below_threshold", 2: "single_wave", 3: "no_feasible_offset",
+                4: "empty"}
+
+
+class TokenWeaveError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class SplitProblem(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int64), ("tokens_per_cta", ctypes.c_int64),
+                ("ctas_per_token_tile", ctypes.c_int64), ("num_cus", ctypes.c_int32),
+                ("ctas_per_cu", ctypes.c_int32), ("min_split_tokens", ctypes.c_int64),
+                ("offsets", ctypes.POINTER(ctypes.c_int32)), ("num_offsets", ctypes.c_int32)]
+
+
+class SplitPlanResult(ctypes.Structure):
+    _fields_ = [("prefix_tokens", ctypes.c_int64), ("suffix_tokens", ctypes.c_int64),
+                ("offset", ctypes.c_int32), ("waves_unsplit", ctypes.c_int32),
+                ("waves_prefix", ctypes.c_int32), ("waves_suffix", ctypes.c_int32),
+                ("reason", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m reduce_rmsnorm_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    common = [ctypes.POINTER(vp), i32, vp, vp, vp, vp, i64, i64, ctypes.c_float, ctypes.c_int]
+    lib.tw_fused_reduce_rmsnorm.argtypes = common + [vp]
+    lib.tw_fused_reduce_rmsnorm.restype = ctypes.c_int
+    lib.tw_shard_rmsnorm.argtypes = common + [i32, vp]
+    lib.tw_shard_rmsnorm.restype = ctypes.c_int
+    lib.tw_split_plan.argtypes = [ctypes.POINTER(SplitProblem), ctypes.POINTER(SplitPlanResult)]
+    lib.tw_split_plan.restype = ctypes.c_int
+    lib.tw_status_string.argtypes = [ctypes.c_int]
+    lib.tw_status_string.restype = ctypes.c_char_p
+    lib.tw_last_error.argtypes = []
+    lib.tw_last_error.restype = ctypes.c_char_p
+    lib.tw_abi_version.argtypes = []
+    lib.tw_abi_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def declared_functions(header: str = HEADER_PATH):
+    """Names of the functions ``include/tokenweave.h`` declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tw_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(status: int) -> None:
+    if status != TW_OK:
+        lib = load_library()
+        raise TokenWeaveError(status, lib.tw_last_error().decode(errors="replace"))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TW_BF16
+    if t.dtype == torch.float32:
+        return TW_F32
+    raise ValueError(f"unsupported dtype {t.dtype}; expected torch.bfloat16 or torch.float32")
+
+
+def _as_list(partials: Union[torch.Tensor, Sequence[torch.Tensor]]):
+    if isinstance(partials, torch.Tensor):
+        if partials.dim() != 3:
+            raise ValueError("a stacked partials tensor must be [N, T, h]")
+        return [partials[i] for i in range(partials.shape[0])]
+    return list(partials)
+
+
+def _marshal(partials, residual, weight, out, residual_out):
+    parts = _as_list(partials)
+    if not parts:
+        raise ValueError("at least one partial is required")
+    if residual.dim() != 2:
+        raise ValueError("residual must be [T, h]")
+    T, h = residual.shape
+    for t in parts + [residual, weight]:
+        if not t.is_cuda:
+            raise ValueError("every tensor must be on a GPU (there is no CPU path)")
+        if t.dtype != residual.dtype:
+            raise ValueError("every tensor must share one dtype")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    for p in parts:
+        if tuple(p.shape) != (T, h):
+            raise ValueError(f"partial shape {tuple(p.shape)} != residual shape {(T, h)}")
+    if tuple(weight.shape) != (h,):
+        raise ValueError("weight must be [h]")
+    if out is None:
+        out = torch.empty_like(residual)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    for t in (out, residual_out):
+        if tuple(t.shape) != (T, h) or t.dtype != residual.dtype or not t.is_contiguous() \
+                or t.device != residual.device:
+            raise ValueError("out and residual_out must be contiguous [T, h] tensors like residual")
+    ptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
+    return parts, ptrs, T, h, out, residual_out
+
+
+def _stream_handle(device: torch.device, stream: Optional[torch.cuda.Stream]):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def tw_fused_reduce_rmsnorm(partials, residual: torch.Tensor, weight: torch.Tensor, eps: float,
+                            out: Optional[torch.Tensor] = None,
+                            residual_out: Optional[torch.Tensor] = None,
+                            stream: Optional[torch.cuda.Stream] = None):
+    """Fused reduce + residual-add + RMSNorm over every row; returns
+    ``(out, residual_out)``.  ``partials`` is a list of [T, h] tensors or one
+    stacked [N, T, h] tensor."""
+    lib = load_library()
+    parts, ptrs, T, h, out, residual_out = _marshal(partials, residual, weight, out, residual_out)
+    with torch.cuda.device(residual.device):
+        _check(lib.tw_fused_reduce_rmsnorm(ptrs, len(parts), residual.data_ptr(), weight.data_ptr(),
+                                           out.data_ptr(), residual_out.data_ptr(), T, h,
+                                           float(eps), _dtype_code(residual),
+                                           _stream_handle(residual.device, stream)))
+    return out, residual_out
+
+
+def tw_shard_rmsnorm(partials, residual: torch.Tensor, weight: torch.Tensor, eps: float,
+                     shard_index: int, out: Optional[torch.Tensor] = None,
+                     residual_out: Optional[torch.Tensor] = None,
+                     stream: Optional[torch.cuda.Stream] = None):
+    """The fused step on rows [floor(k*T/N), floor((k+1)*T/N)) of full-size
+    buffers (N = number of partials); other rows of out/residual_out are left
+    as they were."""
+    lib = load_library()
+    parts, ptrs, T, h, out, residual_out = _marshal(partials, residual, weight, out, residual_out)
+    with torch.cuda.device(residual.device):
+        _check(lib.tw_shard_rmsnorm(ptrs, len(parts), residual.data_ptr(), weight.data_ptr(),
+                                    out.data_ptr(), residual_out.data_ptr(), T, h, float(eps),
+                                    _dtype_code(residual), int(shard_index),
+                                    _stream_handle(residual.device, stream)))
+    return out, residual_out
+
+
+def tw_split_plan(num_tokens: int, tokens_per_cta: int = 1, ctas_per_token_tile: int = 1,
+                  num_cus: int = 256, ctas_per_cu: int = 1, min_split_tokens: int = 0,
+                  offsets: Optional[Sequence[int]] = None) -> dict:
+    """Wave-aware prefix/suffix split plan (host only)."""
+    lib = load_library()
+    arr = None
+    if offsets is not None:
+        arr = (ctypes.c_int32 * len(offsets))(*offsets)
+    prob = SplitProblem(num_tokens, tokens_per_cta, ctas_per_token_tile, num_cus, ctas_per_cu,
+                        min_split_tokens,
+                        ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)) if arr is not None else None,
+                        len(offsets) if offsets is not None else 0)
+    res = SplitPlanResult()
+    _check(lib.tw_split_plan(ctypes.byref(prob), ctypes.byref(res)))
+    return {f: getattr(res, f) for f, _ in SplitPlanResult._fields_}
+
+
+def tw_fused_reduce_rmsnorm_split(partials, residual: torch.Tensor, weight: torch.Tensor,
+                                  eps: float, prefix_tokens: int,
+                                  out: Optional[torch.Tensor] = None,
+                                  residual_out: Optional[torch.Tensor] = None,
+                                  stream: Optional[torch.cuda.Stream] = None):
+    """Split execution: two launches, rows [0, P) then [P, T), on one stream.
+    The suffix launch gets every pointer advanced by P rows."""
+    parts = _as_list(partials)
+    T = residual.shape[0]
+    if not 0 <= prefix_tokens <= T:
+        raise ValueError("prefix_tokens must lie in [0, T]")
+    if out is None:
+        out = torch.empty_like(residual)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    P = int(prefix_tokens)
+    for lo, hi in ((0, P), (P, T)):
+        tw_fused_reduce_rmsnorm([p[lo:hi] for p in parts], residual[lo:hi], weight, eps,
+                                out=out[lo:hi], residual_out=residual_out[lo:hi], stream=stream)
+    return out, residual_out

@@ -1,0 +1,36 @@
+// Internal interface between the C ABI (api.cpp, host-only C++) and the HIP
+// kernels (fused_reduce_rmsnorm.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace tw {
+
+constexpr int kMaxPartials = 16;
+
+struct FusedLaunch {
+  const void* partials[kMaxPartials];
+  int32_t num_partials;
+  const void* residual;
+  const void* weight;
+  void* out;
+  void* residual_out;
+  int64_t row_begin;   // first row this launch processes
+  int64_t num_rows;    // rows processed: [row_begin, row_begin + num_rows)
+  int64_t hidden;
+  float eps;
+  int32_t dtype;       // tw_dtype value
+  void* stream;        // hipStream_t
+};
+
+// Enqueues the kernel.  Returns 0 on success; otherwise writes a message to
+// err (NUL-terminated, at most errlen bytes) and returns a nonzero HIP error.
+int launch_fused(const FusedLaunch& a, char* err, size_t errlen);
+
+// Threads per workgroup and 16-byte vectors per thread that the kernel uses
+// for a given hidden size and element size.  Depends on nothing else, so every
+// launch over rows of the same width runs the same per-row code.
+void kernel_geometry(int64_t hidden, int32_t elem_bytes, int* block, int* vecs_per_thread);
+
+}  // namespace tw

@@ -1,0 +1,196 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function
+the header declares, rejects every invalid argument before touching the
+device, and its split planner matches the oracle bit for bit.
+
+No call here reaches a kernel launch: each fused/shard call carries at least
+one invalid argument, or num_tokens == 0 (a documented no-op)."""
+
+import ctypes
+import random
+import subprocess
+
+import pytest
+
+import oracle
+import reduce_rmsnorm_amd as tw
+from reduce_rmsnorm_amd import _lib
+
+INVALID, UNSUPPORTED = _lib.TW_ERR_INVALID_ARG, _lib.TW_ERR_UNSUPPORTED
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tw.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = tw.declared_functions()
+    assert set(names) >= {"tw_fused_reduce_rmsnorm", "tw_shard_rmsnorm", "tw_split_plan",
+                          "tw_status_string", "tw_last_error", "tw_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    dyn = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in dyn.splitlines() if " T " in ln}
+    assert set(names) <= exported
+    assert lib.tw_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for s in range(4):
+        assert lib.tw_status_string(s).startswith(b"TW_")
+    assert lib.tw_status_string(99) == b"unknown tw_status"
+
+
+# ------------------------------------------------------------ validation ----
+
+A = 0x7F0000000000          # fake, 16-byte aligned "device" addresses (never dereferenced)
+MB = 1 << 20
+
+
+def _call(lib, n=2, T=4, h=64, eps=1e-5, dtype=1, parts=None, res=A + 10 * MB, w=A + 11 * MB,
+          out=A + 12 * MB, rout=A + 13 * MB, shard=None):
+    if parts is None:
+        parts = [A + i * MB for i in range(n)]
+    arr = (ctypes.c_void_p * max(1, len(parts)))(*parts) if parts is not False else None
+    args = [arr, n, res, w, out, rout, T, h, ctypes.c_float(eps), dtype]
+    if shard is None:
+        return lib.tw_fused_reduce_rmsnorm(*args, None)
+    return lib.tw_shard_rmsnorm(*args, shard, None)
+
+
+@pytest.mark.parametrize("shard", [None, 0])
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(n=0, parts=[A]), INVALID, "num_partials"),
+    (dict(n=17, parts=[A + i * MB for i in range(17)]), INVALID, "num_partials"),
+    (dict(T=-1), INVALID, "num_tokens"),
+    (dict(h=0), INVALID, "hidden"),
+    (dict(eps=-1e-5), INVALID, "eps"),
+    (dict(eps=float("inf")), INVALID, "eps"),
+    (dict(eps=float("nan")), INVALID, "eps"),
+    (dict(dtype=7), INVALID, "dtype"),
+    (dict(h=12), UNSUPPORTED, "multiple"),              # bf16 needs h % 8 == 0
+    (dict(h=6, dtype=0), UNSUPPORTED, "multiple"),      # fp32 needs h % 4 == 0
+    (dict(h=65544), UNSUPPORTED, "exceeds"),
+    (dict(h=32772, dtype=0), UNSUPPORTED, "exceeds"),
+    (dict(T=2 ** 31), UNSUPPORTED, "exceeds"),
+    (dict(parts=False), INVALID, "NULL"),
+    (dict(parts=[A, 0]), INVALID, "partials[1] is NULL"),
+    (dict(res=0), INVALID, "NULL"),
+    (dict(w=0), INVALID, "NULL"),
+    (dict(out=0), INVALID, "NULL"),
+    (dict(rout=0), INVALID, "NULL"),
+    (dict(parts=[A, A + MB + 8]), UNSUPPORTED, "aligned"),
+    (dict(res=A + 10 * MB + 4), UNSUPPORTED, "aligned"),
+    (dict(w=A + 11 * MB + 2), UNSUPPORTED, "aligned"),
+    (dict(out=A + 12 * MB + 8), UNSUPPORTED, "aligned"),
+    (dict(rout=A + 13 * MB + 8), UNSUPPORTED, "aligned"),
+    (dict(out=A + 13 * MB + 16), INVALID, "out and residual_out overlap"),
+    (dict(out=A), INVALID, "out overlaps an input (a partial)"),
+    (dict(out=A + 10 * MB + 256), INVALID, "out overlaps an input (residual)"),
+    (dict(out=A + 11 * MB), INVALID, "out overlaps an input (weight)"),
+    (dict(rout=A + MB), INVALID, "residual_out overlaps an input (a partial)"),
+    (dict(rout=A + 10 * MB + 16), INVALID, "residual_out overlaps an input (residual)"),
+    (dict(rout=A + 11 * MB - 16), INVALID, "residual_out overlaps an input (weight)"),
+])
+def test_invalid_arguments_rejected_before_any_device_call(lib, kw, code, needle, shard):
+    assert _call(lib, shard=shard, **kw) == code
+    assert needle in lib.tw_last_error().decode()
+
+
+def test_shard_index_range(lib):
+    for k in (-1, 2, 100):
+        assert _call(lib, shard=k) == INVALID
+        assert b"shard_index" in lib.tw_last_error()
+
+
+def test_empty_batch_is_a_noop(lib):
+    # T == 0 returns OK without looking at the pointers (and without a launch).
+    assert _call(lib, T=0, parts=[0, 0], res=0, w=0, out=0, rout=0) == 0
+    assert _call(lib, T=0, parts=[0, 0], res=0, w=0, out=0, rout=0, shard=1) == 0
+
+
+def test_adjacent_buffers_do_not_overlap(lib):
+    # T*h*2 = 512 bytes: a tensor ending where the next begins is not an overlap;
+    # still invalid elsewhere (eps) so nothing launches.
+    T, h = 4, 64
+    nb = T * h * 2
+    r = _call(lib, T=T, h=h, parts=[A, A + nb], res=A + 2 * nb, w=A + 3 * nb,
+              out=A + 3 * nb + h * 2, rout=A + 4 * nb + h * 2, eps=-1.0)
+    assert r == INVALID and b"eps" in lib.tw_last_error()
+
+
+def test_in_place_residual_is_allowed_by_validation(lib):
+    # residual_out == residual passes the overlap check; eps makes it fail later.
+    assert _call(lib, rout=A + 10 * MB, eps=-1.0) == INVALID
+    assert b"eps" in lib.tw_last_error()
+
+
+# --------------------------------------------------------------- planner ----
+
+def _both(T, **kw):
+    return tw.tw_split_plan(T, **kw), oracle.split_plan(T, **kw)
+
+
+def test_planner_matches_oracle_exhaustive():
+    for S in (132, 256, 7, 1):
+        for T in range(0, 601):
+            got, want = _both(T, num_cus=S)
+            assert got == want, (S, T)
+
+
+def test_planner_matches_oracle_random_tile_models():
+    rng = random.Random(11)
+    for _ in range(3000):
+        kw = dict(tokens_per_cta=rng.choice([1, 16, 64, 128, 256]),
+                  ctas_per_token_tile=rng.choice([1, 2, 8, 32, 64]),
+                  num_cus=rng.choice([1, 8, 132, 256, 304]),
+                  ctas_per_cu=rng.choice([1, 2, 4]),
+                  min_split_tokens=rng.choice([0, 1024, 4096]))
+        if rng.random() < 0.3:
+            kw["offsets"] = sorted(rng.sample(range(0, 1500), rng.randint(0, 8)))
+        T = rng.choice([rng.randint(0, 70000), rng.randint(0, 5000), 2 ** rng.randint(0, 16)])
+        got, want = _both(T, **kw)
+        assert got == want, (T, kw)
+
+
+def test_planner_workload_tile_model():
+    # GEMM tile model used for the Qwen2.5-72B-shaped split: 256x256 tiles over
+    # 8192 output features (32 tiles), one CTA per CU, 256 CUs.
+    p = tw.tw_split_plan(4096, tokens_per_cta=256, ctas_per_token_tile=32, num_cus=256,
+                         min_split_tokens=1024)
+    assert (p["prefix_tokens"], p["suffix_tokens"], p["offset"], p["reason"]) == (2048, 2048, 0, 0)
+    p = tw.tw_split_plan(1024, tokens_per_cta=256, ctas_per_token_tile=32, num_cus=256,
+                         min_split_tokens=1024)
+    assert p["reason"] == 2
+
+
+@pytest.mark.parametrize("kw", [
+    dict(num_tokens=-1), dict(tokens_per_cta=0), dict(ctas_per_token_tile=0), dict(num_cus=0),
+    dict(ctas_per_cu=0), dict(min_split_tokens=-5), dict(offsets=[0, 64, 64]),
+    dict(offsets=[64, 0]), dict(offsets=[-64, 0]),
+])
+def test_planner_invalid(kw):
+    args = dict(num_tokens=100)
+    args.update(kw)
+    T = args.pop("num_tokens")
+    with pytest.raises(tw.TokenWeaveError) as e:
+        tw.tw_split_plan(T, **args)
+    assert e.value.status == INVALID
+
+
+def test_planner_null_and_limits(lib):
+    res = _lib.SplitPlanResult()
+    assert lib.tw_split_plan(None, ctypes.byref(res)) == INVALID
+    prob = _lib.SplitProblem(10, 1, 1, 256, 1, 0, None, 3)      # NULL offsets with a length
+    assert lib.tw_split_plan(ctypes.byref(prob), ctypes.byref(res)) == INVALID
+    assert lib.tw_split_plan(ctypes.byref(prob), None) == INVALID
+    with pytest.raises(tw.TokenWeaveError) as e:
+        tw.tw_split_plan(2 ** 41)
+    assert e.value.status == UNSUPPORTED
+    with pytest.raises(tw.TokenWeaveError) as e:
+        tw.tw_split_plan(10, ctas_per_token_tile=2 ** 21)
+    assert e.value.status == UNSUPPORTED
+    with pytest.raises(tw.TokenWeaveError) as e:    # 2^40 waves do not fit int32
+        tw.tw_split_plan(2 ** 40, num_cus=1)
+    assert e.value.status == UNSUPPORTED

@@ -1,0 +1,225 @@
+"""Parity of the HIP path (called through the C ABI) with the float64 oracle,
+element by element, on seeded inputs; bit-identity invariants; edge cases.
+
+Every kernel launch here is preceded by a flushed line naming the case."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import reduce_rmsnorm_amd as tw
+from synthetic import WORKLOADS, integer_scaled_inputs, make_inputs, special_rows_inputs
+from tests._gpu_util import check, to_device, to_host, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    tw.load_library()
+    torch.cuda.init()
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _run_full(parts, res, w, eps):
+    out, rout = tw.tw_fused_reduce_rmsnorm(parts, res, w, eps)
+    torch.cuda.synchronize()
+    return to_host(out), to_host(rout)
+
+
+def _oracle(d, rows=None):
+    return oracle.fused_reduce_rmsnorm(list(d["partials"]), d["residual"], d["weight"], d["eps"],
+                                       d["dtype"], rows=rows)
+
+
+# ------------------------------------------------------------- workloads ----
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_full_mode_matches_oracle(name):
+    d = make_inputs(name)
+    wl = d["workload"]
+    say(f"full {name}: T={wl.num_tokens} h={wl.hidden} N={wl.num_partials} {wl.dtype} seed={wl.index}")
+    parts, res, w = upload(d)
+    out, rout = _run_full(parts, res, w, d["eps"])
+    y, x, _ = _oracle(d)
+    n_y = check(out, y, d["dtype"], f"{name} out")
+    n_x = check(rout, x, d["dtype"], f"{name} residual_out")
+    say(f"{name}: out not bit-exact {n_y}/{y.size}, residual_out not bit-exact {n_x}/{x.size}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama70b", "mixtral", "llama405b"])
+def test_shard_mode_matches_full_and_leaves_other_rows(name):
+    d = make_inputs(name)
+    wl = d["workload"]
+    N, T = wl.num_partials, wl.num_tokens
+    parts, res, w = upload(d)
+    say(f"full {name} (reference for shards)")
+    out_full, rout_full = _run_full(parts, res, w, d["eps"])
+    y, x, _ = _oracle(d) if name != "llama405b" else (None, None, None)
+    for k in range(N):
+        rows = oracle.shard_rows(T, N, k)
+        out = torch.full_like(res, float("nan"))
+        rout = torch.full_like(res, float("nan"))
+        say(f"shard {name} k={k} rows [{rows.start}, {rows.stop})")
+        tw.tw_shard_rmsnorm(parts, res, w, d["eps"], k, out=out, residual_out=rout)
+        torch.cuda.synchronize()
+        o, r = to_host(out), to_host(rout)
+        sl = slice(rows.start, rows.stop)
+        np.testing.assert_array_equal(o[sl], out_full[sl])      # bit-identical to full mode
+        np.testing.assert_array_equal(r[sl], rout_full[sl])
+        if y is not None:
+            check(o[sl], y[sl], d["dtype"], f"{name} shard {k} out")
+            check(r[sl], x[sl], d["dtype"], f"{name} shard {k} residual_out")
+        other = np.ones(T, bool)
+        other[sl] = False
+        canary = oracle.bf16_bits_to_f64(o[other]) if d["dtype"] == "bf16" else o[other]
+        assert np.isnan(canary).all()
+        canary = oracle.bf16_bits_to_f64(r[other]) if d["dtype"] == "bf16" else r[other]
+        assert np.isnan(canary).all()
+
+
+def test_split_launches_equal_one_launch_for_every_offset():
+    d = make_inputs("qwen72b")
+    T = d["workload"].num_tokens
+    parts, res, w = upload(d)
+    say("full qwen72b (reference for splits)")
+    out_full, rout_full = _run_full(parts, res, w, d["eps"])
+    plan = tw.tw_split_plan(T, tokens_per_cta=256, ctas_per_token_tile=32, num_cus=256,
+                            min_split_tokens=1024)
+    assert plan == oracle.split_plan(T, tokens_per_cta=256, ctas_per_token_tile=32, num_cus=256,
+                                     min_split_tokens=1024)
+    prefixes = sorted({T // 2 + off for off in oracle.DEFAULT_OFFSETS} | {plan["prefix_tokens"]})
+    for P in prefixes:
+        say(f"split qwen72b prefix={P} suffix={T - P}")
+        out, rout = tw.tw_fused_reduce_rmsnorm_split(parts, res, w, d["eps"], P)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_host(out), out_full)
+        np.testing.assert_array_equal(to_host(rout), rout_full)
+
+
+# --------------------------------------------------- shapes and tails ----
+
+RAGGED = [
+    # (N, T, h, dtype): h chosen so the row does not fill the kernel's tiles
+    (1, 1, 8, "bf16"), (3, 5, 264, "bf16"), (2, 33, 1032, "bf16"), (5, 7, 2056, "bf16"),
+    (8, 9, 4104, "bf16"), (8, 3, 8200, "bf16"), (16, 2, 16392, "bf16"), (4, 2, 24584, "bf16"),
+    (2, 3, 65536, "bf16"), (16, 3, 65528, "bf16"),
+    (1, 3, 4, "f32"), (2, 17, 516, "f32"), (7, 4, 1028, "f32"), (16, 5, 2052, "f32"),
+    (3, 2, 32768, "f32"), (2, 2, 32764, "f32"),
+]
+
+
+@pytest.mark.parametrize("N,T,h,dtype", RAGGED)
+def test_ragged_and_extreme_shapes(N, T, h, dtype):
+    wl = WORKLOADS["llama70b"] if dtype == "bf16" else WORKLOADS["tiny"]
+    d = make_inputs(wl, num_tokens=T, hidden=h)
+    d["partials"] = d["partials"][:N] if N <= len(d["partials"]) else np.concatenate(
+        [d["partials"]] * (N // len(d["partials"]) + 1))[:N]
+    say(f"ragged N={N} T={T} h={h} {dtype}")
+    parts, res, w = upload(d)
+    out, rout = _run_full(parts, res, w, d["eps"])
+    y, x, _ = _oracle(d)
+    check(out, y, dtype, "out")
+    check(rout, x, dtype, "residual_out")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_closed_form_rows(dtype):
+    N, T, h = 3, 66, 1024
+    s = special_rows_inputs(N, T, h, dtype)
+    parts = to_device(s["partials"], dtype)
+    res = to_device(s["residual"], dtype)
+    for wkey in ("weight_one", "weight"):
+        say(f"closed-form rows {dtype} {wkey}")
+        w = to_device(s[wkey], dtype)
+        out, rout = _run_full(parts, res, w, 1e-5)
+        y, x, _ = oracle.fused_reduce_rmsnorm(list(s["partials"]), s["residual"], s[wkey], 1e-5, dtype)
+        check(out, y, dtype, "out")
+        check(rout, x, dtype, "residual_out")
+        zero = s["kind"] == 0
+        assert np.all(out[zero] == 0) and np.all(rout[zero] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_exact_sums_invariants(dtype):
+    N, T, h = 8, 40, 8192
+    d = integer_scaled_inputs(N, T, h, dtype, kmax=8)
+    d["eps"] = 1e-5
+    parts, res, w = upload(d)
+    say(f"integer-scaled {dtype}: base")
+    out, rout = _run_full(parts, res, w, 1e-5)
+    y, x, _ = _oracle(d)
+    # sums of k/16 are exact, so residual_out is exactly the rounded sum
+    want_x = oracle.round_f64_to_bf16_bits(x) if dtype == "bf16" else x.astype(np.float32)
+    np.testing.assert_array_equal(rout, want_x)
+    check(out, y, dtype, "out")
+    say(f"integer-scaled {dtype}: permuted partials")
+    perm = [3, 0, 7, 1, 6, 2, 5, 4]
+    out_p, rout_p = _run_full([parts[i] for i in perm], res, w, 1e-5)
+    np.testing.assert_array_equal(out_p, out)
+    np.testing.assert_array_equal(rout_p, rout)
+    say(f"integer-scaled {dtype}: negated inputs")
+    out_n, rout_n = _run_full(-parts, -res, w, 1e-5)
+    # Values compare with +0 == -0: an exactly cancelling sum is +0 under
+    # round-to-nearest whatever the signs of its terms, in the oracle too.
+    val = oracle.bf16_bits_to_f64 if dtype == "bf16" else (lambda a: a.astype(np.float64))
+    np.testing.assert_array_equal(val(out_n), -val(out))
+    np.testing.assert_array_equal(val(rout_n), -val(rout))
+    say(f"integer-scaled {dtype}: doubled weight")
+    out_2, _ = _run_full(parts, res, w * 2, 1e-5)
+    dbl = (lambda a: to_host(to_device(a, dtype) * 2))
+    np.testing.assert_array_equal(out_2, dbl(out))
+
+
+def test_in_place_residual_and_nondefault_stream():
+    d = make_inputs("llama70b", num_tokens=64, hidden=8192)
+    parts, res, w = upload(d)
+    say("in-place reference")
+    out_ref, rout_ref = _run_full(parts, res, w, d["eps"])
+    s = torch.cuda.Stream()
+    say("in-place residual on a side stream")
+    with torch.cuda.stream(s):
+        out, rout = tw.tw_fused_reduce_rmsnorm(parts, res, w, d["eps"], residual_out=res)
+    s.synchronize()
+    assert rout.data_ptr() == res.data_ptr()
+    np.testing.assert_array_equal(to_host(out), out_ref)
+    np.testing.assert_array_equal(to_host(res), rout_ref)
+
+
+def test_empty_and_tiny_batches():
+    d = make_inputs("llama70b", num_tokens=3, hidden=512)
+    parts, res, w = upload(d)
+    out = torch.full_like(res, 7.0)
+    say("shard of an empty range (T=3 < N=8, k=0)")
+    tw.tw_shard_rmsnorm(parts, res, w, d["eps"], 0, out=out, residual_out=torch.empty_like(res))
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+    say("T=0 full mode")
+    e = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
+    o, r = tw.tw_fused_reduce_rmsnorm([e] * 8, e, w, d["eps"])
+    assert o.shape == (0, 512)
+    say("T=3 full mode")
+    out, rout = _run_full(parts, res, w, d["eps"])
+    y, x, _ = _oracle(d)
+    check(out, y, "bf16", "out")
+    check(rout, x, "bf16", "residual_out")
+
+
+def test_zero_row_with_zero_eps_is_nan_documented():
+    # eps = 0 and an all-zero row: 0 * rsqrt(0) = 0 * inf = NaN (documented).
+    parts = torch.zeros((1, 2, 64), dtype=torch.float32, device="cuda")
+    res = torch.zeros((2, 64), dtype=torch.float32, device="cuda")
+    res[1] = 1.0
+    w = torch.ones(64, dtype=torch.float32, device="cuda")
+    say("zero row with eps=0")
+    out, _ = tw.tw_fused_reduce_rmsnorm(parts, res, w, 0.0)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[0]).all() and torch.all(out[1] == 1.0)
