@@ -59,42 +59,81 @@ def parse():
                     help="input sets to rotate through (0: enough to exceed 2x the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget of the CPU oracle sample (0 disables the cpu_baseline leg)")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="also run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="also time the bandwidth probes on the same buffers: N+1 streamed reads "
+                         "+ 2 streamed writes, reads only, writes only (the achievable envelope; "
+                         "their known byte counts also calibrate the hardware counters)")
     return ap.parse_args()
 
 
+def run_ceiling(sets, R, rows, h, itemsize, stream, steps, timer):
+    """Time the measurement-only probes of libtw_bwprobe.so over the bench's
+    own rotated buffers: sources are the partial rows and the residual rows,
+    destinations are out and residual_out."""
+    import ctypes
+    from reduce_rmsnorm_amd.build import PROBE_LIB_PATH
+    lib = ctypes.CDLL(PROBE_LIB_PATH)
+    lib.tw_probe_launch.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int64,
+                                    ctypes.c_int, ctypes.c_void_p]
+    lib.tw_probe_launch.restype = ctypes.c_int
+    tensor_bytes = rows * h * itemsize
+    nvec = tensor_bytes // 16
+    ptrs = []
+    for parts, res, out, rout in sets:
+        src = [parts[i, :rows].data_ptr() for i in range(parts.shape[0])] + [res[:rows].data_ptr()]
+        dst = [out.data_ptr(), rout.data_ptr()]
+        ptrs.append(((ctypes.c_void_p * len(src))(*src), len(src), (ctypes.c_void_p * 2)(*dst)))
+    nsrc = ptrs[0][1]
+    res = {"tensor_bytes": tensor_bytes, "grid": 2048}
+    for kind, key, nbytes in ((0, "read_write", (nsrc + 2) * tensor_bytes),
+                              (1, "read_only", nsrc * tensor_bytes),
+                              (2, "write_only", 2 * tensor_bytes)):
+        def go(i, kind=kind):
+            src, n, dst = ptrs[i % R]
+            rc = lib.tw_probe_launch(kind, src, n, dst, 2, nvec, 2048, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed: {rc}")
+        us = timer(go, steps)
+        res[key + "_us"] = round(us, 3)
+        res[key + "_bytes"] = nbytes
+        res[key + "_gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+        print(f"[bench] probe {key}: {nbytes} B in {us:.2f} us = {res[key + '_gbs']} GB/s",
+              file=sys.stderr, flush=True)
+    return res
+
+
 def cpu_baseline(wl, d, budget_s: float) -> dict:
-    """Time the float64 oracle as it stands on whole rows of the same batch,
-    pinned to one host core, until the budget is spent or all rows are done."""
-    import numpy as np  # noqa: F401
+    """Time the float64 oracle as it stands, pinned to one host core, on
+    whole rows of the same batch: passes over the batch, 8 rows at a time,
+    until the time budget is spent (the last chunk is finished)."""
     import oracle
     parts = list(d["partials"])
     T = wl.num_tokens
     try:
         saved = os.sched_getaffinity(0)
-        core = min(saved)
-        os.sched_setaffinity(0, {core})
+        os.sched_setaffinity(0, {min(saved)})
     except (AttributeError, OSError):
         saved = None
     try:
         rows_done = 0
         t0 = time.perf_counter()
         chunk = 8
-        while rows_done < T and time.perf_counter() - t0 < budget_s:
-            rows = range(rows_done, min(T, rows_done + chunk))
+        while time.perf_counter() - t0 < budget_s:
+            lo = rows_done % T
+            rows = range(lo, min(T, lo + chunk))
             oracle.fused_reduce_rmsnorm(parts, d["residual"], d["weight"], d["eps"], wl.dtype,
                                         rows=rows)
-            rows_done = rows.stop
+            rows_done += len(rows)
         elapsed = time.perf_counter() - t0
     finally:
         if saved is not None:
             os.sched_setaffinity(0, saved)
     gbs = wl.algorithmic_bytes(rows_done) / elapsed / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows_done} of {T} rows of the same {wl.name} batch, float64 NumPy "
-                      f"oracle, one pass, {elapsed:.1f} s on 1 pinned core of "
-                      f"{len(saved) if saved else os.cpu_count()}",
+            "sample": f"{rows_done} rows ({rows_done / T:.1f} passes over the {T}-row "
+                      f"{wl.name} batch), float64 NumPy oracle, {elapsed:.1f} s on 1 pinned "
+                      f"core of {len(saved) if saved else os.cpu_count()}",
             "tokens_per_s": round(rows_done / elapsed, 1)}
 
 
@@ -181,14 +220,21 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms, {ms_per_step * 1e3:.2f} us/step, "
           f"{gbs:.1f} GB/s", file=sys.stderr, flush=True)
 
-    if args.copy_probe:
-        n = 512 * 1024 * 1024
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] copy probe: 5 x {n} bytes device-to-device", file=sys.stderr, flush=True)
+    ceiling = None
+    if args.ceiling:
+        def timer(go, k):
+            for i in range(min(20, k)):
+                go(i)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(k):
+                go(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / k
+        ceiling = run_ceiling(sets, R, rows, h, wl.itemsize, stream, min(args.steps, 500), timer)
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE) and args.mode == "full" and wl.name == "llama70b":
@@ -223,6 +269,8 @@ def main():
                      "avg_launch_us": round(ms * 1e3 / max(1, launches), 3)},
         "cpu_baseline": None,
     }
+    if ceiling is not None:
+        result["ceiling"] = ceiling
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, d, args.cpu_seconds)

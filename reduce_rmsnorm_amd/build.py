@@ -32,6 +32,10 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
 HOST_SOURCES = ["api.cpp", "split_plan.cpp"]
 HIP_SOURCES = ["fused_reduce_rmsnorm.hip"]
+# Measurement-only bandwidth probes (bench.py --ceiling, counter calibration),
+# built into a library of their own so the fused library carries none of them.
+PROBE_SOURCE = "bw_probe.hip"
+PROBE_LIB_PATH = os.path.join(PKG, "libtw_bwprobe.so")
 
 
 def _hipcc() -> str:
@@ -75,10 +79,16 @@ def build(verbose: bool = False) -> str:
     if verbose:
         for c in cmds:
             print(" ".join(c))
+    probe_obj = os.path.join(BUILD, PROBE_SOURCE + ".o")
+    cmds.append([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, PROBE_SOURCE), "-o", probe_obj])
+    if verbose:
+        print(" ".join(cmds[-1]))
     _run_all(cmds)
-    tmp = LIB_PATH + ".tmp"
-    _run_all([[hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]])
+    tmp, ptmp = LIB_PATH + ".tmp", PROBE_LIB_PATH + ".tmp"
+    _run_all([[hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs],
+              [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", ptmp, probe_obj]])
     os.replace(tmp, LIB_PATH)
+    os.replace(ptmp, PROBE_LIB_PATH)
     return LIB_PATH
 
 
