@@ -59,6 +59,9 @@ def parse():
                     help="input sets to rotate through (0: enough to exceed 2x the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget of the CPU oracle sample (0 disables the cpu_baseline leg)")
+    ap.add_argument("--no-unfused", dest="unfused", action="store_false",
+                    help="skip timing the unfused comparator (standalone reduce, then a "
+                         "two-pass residual-add + RMSNorm) in full mode")
     ap.add_argument("--ceiling", action="store_true",
                     help="also time the bandwidth probes on the same buffers: N+1 streamed reads "
                          "+ 2 streamed writes, reads only, writes only (the achievable envelope; "
@@ -220,6 +223,37 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms, {ms_per_step * 1e3:.2f} us/step, "
           f"{gbs:.1f} GB/s", file=sys.stderr, flush=True)
 
+    unfused = None
+    if args.mode == "full" and args.unfused:
+        # The reduce-then-normalize sequence the fused kernel replaces, on the
+        # same rotated buffers (plus one intermediate tensor per set).
+        reds = [torch.empty_like(st[1]) for st in sets]
+
+        def ustep(i):
+            parts, res, out, rout = sets[i % R]
+            tw.tw_unfused_reduce_rmsnorm(parts, res, w, wl.eps, out=out, residual_out=rout,
+                                         reduced=reds[i % R], stream=stream)
+
+        for i in range(args.warmup):
+            ustep(i)
+        torch.cuda.synchronize()
+        u0 = torch.cuda.Event(enable_timing=True)
+        u1 = torch.cuda.Event(enable_timing=True)
+        u0.record(stream)
+        for i in range(args.steps):
+            ustep(i)
+        u1.record(stream)
+        torch.cuda.synchronize()
+        u_us = u0.elapsed_time(u1) * 1e3 / args.steps
+        u_bytes = (N + 6) * rows * h * wl.itemsize
+        unfused = {"us_per_step": round(u_us, 3), "launches_per_step": 2,
+                   "traffic_bytes_algorithmic": u_bytes,
+                   "gbs_of_own_traffic": round(u_bytes / (u_us * 1e-6) / 1e9, 1),
+                   "fused_speedup": round(u_us / (ms_per_step * 1e3), 4)}
+        print(f"[bench] unfused comparator: {u_us:.2f} us/step, fused speedup "
+              f"{unfused['fused_speedup']:.3f}x", file=sys.stderr, flush=True)
+        del reds
+
     ceiling = None
     if args.ceiling:
         def timer(go, k):
@@ -269,6 +303,8 @@ def main():
                      "avg_launch_us": round(ms * 1e3 / max(1, launches), 3)},
         "cpu_baseline": None,
     }
+    if unfused is not None:
+        result["unfused_comparator"] = unfused
     if ceiling is not None:
         result["ceiling"] = ceiling
     if args.cpu_seconds > 0:

@@ -127,6 +127,40 @@ tw_status tw_shard_rmsnorm(const void* const* partials, int32_t num_partials,
                            tw_dtype dtype, int32_t shard_index, void* stream);
 
 /*
+ * Unfused comparator (not on the fused path).  [Blog] "What it buys" measures
+ * the fused kernel against a standalone AllReduce followed by a standalone
+ * RMSNorm; [Blog] "Fix two" describes the standard RMSNorm as reading the
+ * tensor twice (once for the variance, once to scale) and writing it once.
+ * These two calls are that sequence on one GPU, for timing against
+ * tw_fused_reduce_rmsnorm: (N+3) reads and 3 writes of [T, h] against the
+ * fused kernel's (N+1) reads and 2 writes.
+ *
+ * tw_reduce_partials -- the AllReduce result:
+ *     reduced[t,:] = round_dtype( sum_{i<N} partials[i][t,:] )
+ * with the fused kernel's compensated float32 sum.
+ *   partials, num_partials, num_tokens, hidden, dtype, stream: as for
+ *                 tw_fused_reduce_rmsnorm
+ *   reduced       device [num_tokens, hidden] `dtype`, written; must not
+ *                 overlap a partial
+ * Errors: those of tw_fused_reduce_rmsnorm that apply to these arguments.
+ */
+tw_status tw_reduce_partials(const void* const* partials, int32_t num_partials, void* reduced,
+                             int64_t num_tokens, int64_t hidden, tw_dtype dtype, void* stream);
+
+/*
+ * tw_add_rmsnorm -- standard two-pass residual-add + RMSNorm.  Per row:
+ *   pass 1: x = input + residual (compensated float32), residual_out =
+ *           round_dtype(x), s = sum_j x_j^2 of the unrounded x;
+ *   pass 2: re-read residual_out, out = round_dtype((x' * rs) * weight) with
+ *           x' the stored (rounded) value and rs = 1/sqrt(s/hidden + eps).
+ * Arguments as for tw_fused_reduce_rmsnorm with one partial (`input`);
+ * residual_out may equal residual exactly.  Same errors.
+ */
+tw_status tw_add_rmsnorm(const void* input, const void* residual, const void* weight, void* out,
+                         void* residual_out, int64_t num_tokens, int64_t hidden, float eps,
+                         tw_dtype dtype, void* stream);
+
+/*
  * Split planner: [Blog] "The overlap trap" and "Fix one".  A GEMM over M
  * token rows launches ceil(M / tokens_per_cta) * ctas_per_token_tile CTAs;
  * a wave holds num_cus * ctas_per_cu of them; waves(M) = ceil(CTAs / that).

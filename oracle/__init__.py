@@ -17,6 +17,10 @@ Sources, named by page title and section:
   (aifetchly), section "Fused AllReduce-RMSNorm: Bypassing Global Memory",
   the RMSNorm equation.
 
+``unfused`` holds the oracle of the unfused comparator (a standalone
+reduction, then a standard two-pass residual-add + RMSNorm), [Blog] sections
+"What it buys" and "Fix two".
+
 Every numeric function is pinned by the ``-m "not gpu"`` tests against closed
 forms, brute force with exact rationals, a library special case and the
 worked wave example the pages print.  No function here is "parity unpinned".
@@ -29,6 +33,11 @@ from .rmsnorm import (  # noqa: F401
     shard_rows,
     fused_reduce_rmsnorm,
     shard_rmsnorm,
+)
+from .unfused import (  # noqa: F401
+    reduce_partials,
+    add_rmsnorm_two_pass,
+    unfused_reduce_rmsnorm,
 )
 from .planner import (  # noqa: F401
     DEFAULT_OFFSETS,

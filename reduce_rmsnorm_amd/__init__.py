@@ -6,7 +6,10 @@ The Python names mirror the C entry points:
 * :func:`tw_fused_reduce_rmsnorm` -- every row,
 * :func:`tw_shard_rmsnorm` -- one rank's token shard,
 * :func:`tw_split_plan` -- the prefix/suffix split plan,
-* :func:`tw_fused_reduce_rmsnorm_split` -- the two launches of a split.
+* :func:`tw_fused_reduce_rmsnorm_split` -- the two launches of a split,
+* :func:`tw_reduce_partials`, :func:`tw_add_rmsnorm` and
+  :func:`tw_unfused_reduce_rmsnorm` -- the unfused comparator (a standalone
+  reduction, then a standard two-pass residual-add + RMSNorm).
 """
 
 from ._lib import (  # noqa: F401
@@ -16,7 +19,10 @@ from ._lib import (  # noqa: F401
     declared_functions,
     load_library,
     tw_fused_reduce_rmsnorm,
+    tw_add_rmsnorm,
     tw_fused_reduce_rmsnorm_split,
+    tw_reduce_partials,
     tw_shard_rmsnorm,
     tw_split_plan,
+    tw_unfused_reduce_rmsnorm,
 )

@@ -69,6 +69,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tw_fused_reduce_rmsnorm.restype = ctypes.c_int
     lib.tw_shard_rmsnorm.argtypes = common + [i32, vp]
     lib.tw_shard_rmsnorm.restype = ctypes.c_int
+    lib.tw_reduce_partials.argtypes = [ctypes.POINTER(vp), i32, vp, i64, i64, ctypes.c_int, vp]
+    lib.tw_reduce_partials.restype = ctypes.c_int
+    lib.tw_add_rmsnorm.argtypes = [vp, vp, vp, vp, vp, i64, i64, ctypes.c_float, ctypes.c_int, vp]
+    lib.tw_add_rmsnorm.restype = ctypes.c_int
     lib.tw_split_plan.argtypes = [ctypes.POINTER(SplitProblem), ctypes.POINTER(SplitPlanResult)]
     lib.tw_split_plan.restype = ctypes.c_int
     lib.tw_status_string.argtypes = [ctypes.c_int]
@@ -178,6 +182,52 @@ def tw_shard_rmsnorm(partials, residual: torch.Tensor, weight: torch.Tensor, eps
                                     _dtype_code(residual), int(shard_index),
                                     _stream_handle(residual.device, stream)))
     return out, residual_out
+
+
+def tw_reduce_partials(partials, reduced: Optional[torch.Tensor] = None,
+                       stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Unfused comparator, step 1: reduced = round(sum of the partials)."""
+    lib = load_library()
+    parts = _as_list(partials)
+    if not parts:
+        raise ValueError("at least one partial is required")
+    ref = parts[0]
+    if ref.dim() != 2:
+        raise ValueError("partials must be [T, h]")
+    weight_stub = ref[0] if ref.shape[0] > 0 else ref.new_empty((ref.shape[1],))
+    parts, ptrs, T, h, reduced, _ = _marshal(parts, ref, weight_stub, reduced, ref)
+    with torch.cuda.device(ref.device):
+        _check(lib.tw_reduce_partials(ptrs, len(parts), reduced.data_ptr(), T, h,
+                                      _dtype_code(ref), _stream_handle(ref.device, stream)))
+    return reduced
+
+
+def tw_add_rmsnorm(inp: torch.Tensor, residual: torch.Tensor, weight: torch.Tensor, eps: float,
+                   out: Optional[torch.Tensor] = None, residual_out: Optional[torch.Tensor] = None,
+                   stream: Optional[torch.cuda.Stream] = None):
+    """Unfused comparator, step 2: standard two-pass residual-add + RMSNorm."""
+    lib = load_library()
+    _, _, T, h, out, residual_out = _marshal([inp], residual, weight, out, residual_out)
+    with torch.cuda.device(residual.device):
+        _check(lib.tw_add_rmsnorm(inp.data_ptr(), residual.data_ptr(), weight.data_ptr(),
+                                  out.data_ptr(), residual_out.data_ptr(), T, h, float(eps),
+                                  _dtype_code(residual), _stream_handle(residual.device, stream)))
+    return out, residual_out
+
+
+def tw_unfused_reduce_rmsnorm(partials, residual: torch.Tensor, weight: torch.Tensor, eps: float,
+                              out: Optional[torch.Tensor] = None,
+                              residual_out: Optional[torch.Tensor] = None,
+                              reduced: Optional[torch.Tensor] = None,
+                              stream: Optional[torch.cuda.Stream] = None):
+    """The unfused sequence: tw_reduce_partials, then tw_add_rmsnorm.
+    Returns (out, residual_out, reduced)."""
+    if reduced is None:
+        reduced = torch.empty_like(residual)
+    tw_reduce_partials(partials, reduced=reduced, stream=stream)
+    out, residual_out = tw_add_rmsnorm(reduced, residual, weight, eps, out=out,
+                                       residual_out=residual_out, stream=stream)
+    return out, residual_out, reduced
 
 
 def tw_split_plan(num_tokens: int, tokens_per_cta: int = 1, ctas_per_token_tile: int = 1,

@@ -31,7 +31,7 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
 HOST_SOURCES = ["api.cpp", "split_plan.cpp"]
-HIP_SOURCES = ["fused_reduce_rmsnorm.hip"]
+HIP_SOURCES = ["fused_reduce_rmsnorm.hip", "unfused.hip"]
 # Measurement-only bandwidth probes (bench.py --ceiling, counter calibration),
 # built into a library of their own so the fused library carries none of them.
 PROBE_SOURCE = "bw_probe.hip"

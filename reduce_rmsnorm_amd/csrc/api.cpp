@@ -39,7 +39,7 @@ Range range_of(const void* p, uint64_t bytes) {
 // valid.  With num_tokens == 0 the pointers are not inspected.
 tw_status validate(const void* const* partials, int32_t n, const void* residual,
                    const void* weight, void* out, void* residual_out, int64_t T, int64_t h,
-                   float eps, tw_dtype dtype, const char* who) {
+                   float eps, tw_dtype dtype, const char* who, bool outputs_alias = false) {
   if (n < 1 || n > TW_MAX_PARTIALS) {
     set_error("%s: num_partials=%d outside [1, %d]", who, n, TW_MAX_PARTIALS);
     return TW_ERR_INVALID_ARG;
@@ -100,12 +100,15 @@ tw_status validate(const void* const* partials, int32_t n, const void* residual,
   const Range r_res_out = range_of(residual_out, tensor_bytes);
   const Range r_res = range_of(residual, tensor_bytes);
   const Range r_w = range_of(weight, (uint64_t)h * es);
-  if (overlaps(r_out, r_res_out)) {
+  if (!outputs_alias && overlaps(r_out, r_res_out)) {
     set_error("%s: out and residual_out overlap", who);
     return TW_ERR_INVALID_ARG;
   }
+  // With outputs_alias the caller has one output (passed as both) and the
+  // residual/weight slots hold a partial; only the partials are checked.
   const bool in_place = residual_out == residual;
-  for (int32_t i = 0; i <= n + 1; ++i) {
+  const int32_t last_input = outputs_alias ? n - 1 : n + 1;
+  for (int32_t i = 0; i <= last_input; ++i) {
     const Range in = i < n ? range_of(partials[i], tensor_bytes) : (i == n ? r_res : r_w);
     if (overlaps(r_out, in)) {
       set_error("%s: out overlaps an input (%s)", who,
@@ -182,6 +185,62 @@ tw_status tw_shard_rmsnorm(const void* const* partials, int32_t num_partials,
   const int64_t hi = ((int64_t)shard_index + 1) * num_tokens / num_partials;
   return tw::launch_rows(partials, num_partials, residual, weight, out, residual_out, lo, hi,
                          hidden, eps, dtype, stream);
+}
+
+tw_status tw_reduce_partials(const void* const* partials, int32_t num_partials, void* reduced,
+                             int64_t num_tokens, int64_t hidden, tw_dtype dtype, void* stream) {
+  // Same checks as the fused entry with the reduced tensor standing in for
+  // both outputs' ranges; a zero eps and the partials as residual/weight
+  // placeholders keep the shared validation meaningful.
+  const char* who = "tw_reduce_partials";
+  if (num_tokens > 0 && reduced == nullptr) {
+    tw::set_error("%s: NULL tensor pointer", who);
+    return TW_ERR_INVALID_ARG;
+  }
+  const void* any = (partials != nullptr && num_partials >= 1) ? partials[0] : nullptr;
+  tw_status s = tw::validate(partials, num_partials, any, any, reduced, reduced, num_tokens,
+                             hidden, 0.0f, dtype, who, /*outputs_alias=*/true);
+  if (s != TW_OK || num_tokens == 0) return s;
+  tw::ReduceLaunch L{};
+  for (int32_t i = 0; i < num_partials; ++i) L.partials[i] = partials[i];
+  L.num_partials = num_partials;
+  L.reduced = reduced;
+  L.num_rows = num_tokens;
+  L.hidden = hidden;
+  L.dtype = (int32_t)dtype;
+  L.stream = stream;
+  char msg[256];
+  if (tw::launch_reduce(L, msg, sizeof(msg)) != 0) {
+    tw::set_error("%s", msg);
+    return TW_ERR_DEVICE;
+  }
+  return TW_OK;
+}
+
+tw_status tw_add_rmsnorm(const void* input, const void* residual, const void* weight, void* out,
+                         void* residual_out, int64_t num_tokens, int64_t hidden, float eps,
+                         tw_dtype dtype, void* stream) {
+  const void* parts[1] = {input};
+  const tw_status s = tw::validate(parts, 1, residual, weight, out, residual_out, num_tokens,
+                                   hidden, eps, dtype, "tw_add_rmsnorm");
+  if (s != TW_OK || num_tokens == 0) return s;
+  tw::AddNormLaunch L{};
+  L.input = input;
+  L.residual = residual;
+  L.weight = weight;
+  L.out = out;
+  L.residual_out = residual_out;
+  L.num_rows = num_tokens;
+  L.hidden = hidden;
+  L.eps = eps;
+  L.dtype = (int32_t)dtype;
+  L.stream = stream;
+  char msg[256];
+  if (tw::launch_add_rmsnorm(L, msg, sizeof(msg)) != 0) {
+    tw::set_error("%s", msg);
+    return TW_ERR_DEVICE;
+  }
+  return TW_OK;
 }
 
 const char* tw_status_string(tw_status s) {

@@ -28,6 +28,33 @@ struct FusedLaunch {
 // err (NUL-terminated, at most errlen bytes) and returns a nonzero HIP error.
 int launch_fused(const FusedLaunch& a, char* err, size_t errlen);
 
+// Unfused comparator: reduced = round(sum of partials), one row per workgroup.
+struct ReduceLaunch {
+  const void* partials[kMaxPartials];
+  int32_t num_partials;
+  void* reduced;
+  int64_t num_rows;
+  int64_t hidden;
+  int32_t dtype;
+  void* stream;
+};
+int launch_reduce(const ReduceLaunch& a, char* err, size_t errlen);
+
+// Unfused comparator: two-pass residual-add + RMSNorm (reads the tensor twice).
+struct AddNormLaunch {
+  const void* input;
+  const void* residual;
+  const void* weight;
+  void* out;
+  void* residual_out;
+  int64_t num_rows;
+  int64_t hidden;
+  float eps;
+  int32_t dtype;
+  void* stream;
+};
+int launch_add_rmsnorm(const AddNormLaunch& a, char* err, size_t errlen);
+
 // Threads per workgroup and 16-byte vectors per thread that the kernel uses
 // for a given hidden size and element size.  Depends on nothing else, so every
 // launch over rows of the same width runs the same per-row code.

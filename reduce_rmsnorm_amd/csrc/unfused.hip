@@ -1,0 +1,241 @@
+// Unfused comparator for gfx950: the reduce-then-normalize sequence that the
+// fused kernel replaces.  The blog post "TokenWeave: Why Hiding
+// Tensor-Parallel Communication Needs Wave Arithmetic, Not Finer Tiles"
+// measures its fused kernel against a standalone AllReduce followed by a
+// standalone RMSNorm (section "What it buys"), and describes the standard
+// RMSNorm as reading the tensor twice, once for the variance and once to
+// scale, and writing it once (section "Fix two: RMSNorm was never
+// insignificant").  On one GPU those two steps are:
+//
+//  reduce_kernel       reduced = round(P_0 + ... + P_{N-1})       N reads, 1 write
+//  add_rmsnorm_kernel  pass 1: x = reduced + R, residual_out = round(x),
+//                              sum of squares of x                 2 reads, 1 write
+//                      pass 2: re-read residual_out, out = (x' * rs) * w
+//                                                                  1 read,  1 write
+//
+// so (N+3) reads and 3 writes against the fused kernel's (N+1) and 2.  The
+// arithmetic matches the fused kernel (compensated float32 sums, correctly
+// rounded stores, the same wave/LDS reduction order, the same geometry table);
+// what differs is the rounding of the intermediate tensors, which the unfused
+// flow stores and reads back.
+
+#include <hip/hip_runtime.h>
+
+#include <array>
+#include <cstdio>
+#include <utility>
+
+#include "device_common.h"
+#include "geometry.h"
+#include "launch.h"
+
+namespace tw {
+namespace {
+
+using namespace dev;
+
+struct ReduceArgs {
+  const u32x4* partials[kMaxPartials];
+  u32x4* reduced;
+  int32_t nvec;
+};
+
+struct AddNormArgs {
+  const u32x4* input;
+  const u32x4* residual;
+  const u32x4* weight;
+  u32x4* out;
+  u32x4* residual_out;
+  int32_t nvec;
+  float hidden;
+  float eps;
+};
+
+template <int N, int BLOCK, int VPT, bool BF16>
+__global__ __launch_bounds__(BLOCK) void reduce_kernel(ReduceArgs a) {
+  constexpr int E = Elem<BF16>::kPerVec;
+  const int tid = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * a.nvec;
+  const int nvec = a.nvec;
+  int vi[VPT];
+  bool valid[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int v = tid + j * BLOCK;
+    valid[j] = v < nvec;
+    vi[j] = valid[j] ? v : nvec - 1;
+  }
+  u32x4 raw[N][VPT];
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+      raw[i][j] = __builtin_nontemporal_load(a.partials[i] + base + vi[j]);
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    float s[E], c[E], t[E], keep[E];
+    unpack<BF16>(raw[0][j], s);
+#pragma unroll
+    for (int e = 0; e < E; ++e) c[e] = 0.0f;
+#pragma unroll
+    for (int i = 1; i < N; ++i) {
+      unpack<BF16>(raw[i][j], t);
+#pragma unroll
+      for (int e = 0; e < E; ++e) two_sum_into(s[e], c[e], t[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float xe = s[e] + c[e];
+      keep[e] = BF16 ? round_to_odd(s[e], c[e], xe) : xe;
+    }
+    if (valid[j]) a.reduced[base + vi[j]] = pack<BF16>(keep);
+  }
+}
+
+template <int BLOCK, int VPT, bool BF16>
+__global__ __launch_bounds__(BLOCK) void add_rmsnorm_kernel(AddNormArgs a) {
+  constexpr int E = Elem<BF16>::kPerVec;
+  constexpr int NW = BLOCK / 64;
+  __shared__ float wave_part[NW];
+  const int tid = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * a.nvec;
+  const int nvec = a.nvec;
+  int vi[VPT];
+  bool valid[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int v = tid + j * BLOCK;
+    valid[j] = v < nvec;
+    vi[j] = valid[j] ? v : nvec - 1;
+  }
+  // Pass 1: x = input + residual, store it, sum of squares of x.
+  u32x4 rin[VPT], rres[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    rin[j] = a.input[base + vi[j]];
+    rres[j] = a.residual[base + vi[j]];
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    float s[E], c[E], t[E], keep[E];
+    unpack<BF16>(rin[j], s);
+    unpack<BF16>(rres[j], t);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      c[e] = 0.0f;
+      two_sum_into(s[e], c[e], t[e]);
+      const float xe = s[e] + c[e];
+      keep[e] = BF16 ? round_to_odd(s[e], c[e], xe) : xe;
+      if (valid[j]) ss = __builtin_fmaf(xe, xe, ss);
+    }
+    if (valid[j]) a.residual_out[base + vi[j]] = pack<BF16>(keep);
+  }
+  const float wsum = wave_sum(ss);
+  if ((tid & 63) == 0) wave_part[tid >> 6] = wsum;
+  __syncthreads();
+  float total = wave_part[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) total += wave_part[w];
+  const float rs = __builtin_amdgcn_rsqf(total / a.hidden + a.eps);
+  // Pass 2: read the stored tensor again and scale it.  Each thread re-reads
+  // only the elements it stored itself; the barrier above (a workgroup-scope
+  // fence) keeps the compiler from forwarding the stored values, so these are
+  // real loads, and a wave's accesses to one address stay in program order.
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const u32x4 xr = a.residual_out[base + vi[j]];
+    const u32x4 wr = a.weight[vi[j]];
+    float x[E], w[E], y[E];
+    unpack<BF16>(xr, x);
+    unpack<BF16>(wr, w);
+#pragma unroll
+    for (int e = 0; e < E; ++e) y[e] = (x[e] * rs) * w[e];
+    if (valid[j]) a.out[base + vi[j]] = pack<BF16>(y);
+  }
+}
+
+using ReduceFn = void (*)(ReduceArgs);
+using AddNormFn = void (*)(AddNormArgs);
+
+template <bool BF16, int G, int... Ns>
+constexpr std::array<ReduceFn, sizeof...(Ns)> reduce_row(std::integer_sequence<int, Ns...>) {
+  return {&reduce_kernel<Ns + 1, kGeometry[G].block, kGeometry[G].vpt, BF16>...};
+}
+template <bool BF16, int... Gs>
+constexpr std::array<std::array<ReduceFn, kMaxPartials>, sizeof...(Gs)> reduce_table(
+    std::integer_sequence<int, Gs...>) {
+  return {reduce_row<BF16, Gs>(std::make_integer_sequence<int, kMaxPartials>{})...};
+}
+template <bool BF16, int... Gs>
+constexpr std::array<AddNormFn, sizeof...(Gs)> addnorm_table(std::integer_sequence<int, Gs...>) {
+  return {&add_rmsnorm_kernel<kGeometry[Gs].block, kGeometry[Gs].vpt, BF16>...};
+}
+
+const auto kReduceF32 = reduce_table<false>(std::make_integer_sequence<int, kNumGeometries>{});
+const auto kReduceBF16 = reduce_table<true>(std::make_integer_sequence<int, kNumGeometries>{});
+const auto kAddNormF32 = addnorm_table<false>(std::make_integer_sequence<int, kNumGeometries>{});
+const auto kAddNormBF16 = addnorm_table<true>(std::make_integer_sequence<int, kNumGeometries>{});
+
+int shape_error(int64_t nvec, int64_t rows, int g, char* err, size_t errlen) {
+  if (g < 0 || nvec > kMaxVectors || rows <= 0 || rows > 0x7FFFFFFF) {
+    std::snprintf(err, errlen, "internal: launch shape outside the compiled kernels");
+    return (int)hipErrorInvalidValue;
+  }
+  return 0;
+}
+
+}  // namespace
+
+int launch_reduce(const ReduceLaunch& L, char* err, size_t errlen) {
+  const bool bf16 = L.dtype == 1;
+  const int64_t nvec = L.hidden * (bf16 ? 2 : 4) / 16;
+  const int g = geometry_index(nvec);
+  if (const int e = shape_error(nvec, L.num_rows, g, err, errlen)) return e;
+  if (L.num_partials < 1 || L.num_partials > kMaxPartials) {
+    std::snprintf(err, errlen, "internal: partial count outside the compiled kernels");
+    return (int)hipErrorInvalidValue;
+  }
+  ReduceArgs k{};
+  for (int i = 0; i < L.num_partials; ++i) k.partials[i] = static_cast<const u32x4*>(L.partials[i]);
+  k.reduced = static_cast<u32x4*>(L.reduced);
+  k.nvec = (int32_t)nvec;
+  const ReduceFn fn = bf16 ? kReduceBF16[g][L.num_partials - 1] : kReduceF32[g][L.num_partials - 1];
+  void* args[] = {&k};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)L.num_rows),
+                                       dim3(kGeometry[g].block), args, 0,
+                                       static_cast<hipStream_t>(L.stream));
+  if (e != hipSuccess) {
+    std::snprintf(err, errlen, "hipLaunchKernel: %s", hipGetErrorString(e));
+    return (int)e;
+  }
+  return 0;
+}
+
+int launch_add_rmsnorm(const AddNormLaunch& L, char* err, size_t errlen) {
+  const bool bf16 = L.dtype == 1;
+  const int64_t nvec = L.hidden * (bf16 ? 2 : 4) / 16;
+  const int g = geometry_index(nvec);
+  if (const int e = shape_error(nvec, L.num_rows, g, err, errlen)) return e;
+  AddNormArgs k{};
+  k.input = static_cast<const u32x4*>(L.input);
+  k.residual = static_cast<const u32x4*>(L.residual);
+  k.weight = static_cast<const u32x4*>(L.weight);
+  k.out = static_cast<u32x4*>(L.out);
+  k.residual_out = static_cast<u32x4*>(L.residual_out);
+  k.nvec = (int32_t)nvec;
+  k.hidden = (float)L.hidden;
+  k.eps = L.eps;
+  const AddNormFn fn = bf16 ? kAddNormBF16[g] : kAddNormF32[g];
+  void* args[] = {&k};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)L.num_rows),
+                                       dim3(kGeometry[g].block), args, 0,
+                                       static_cast<hipStream_t>(L.stream));
+  if (e != hipSuccess) {
+    std::snprintf(err, errlen, "hipLaunchKernel: %s", hipGetErrorString(e));
+    return (int)e;
+  }
+  return 0;
+}
+
+}  // namespace tw

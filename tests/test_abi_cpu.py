@@ -98,6 +98,22 @@ def test_invalid_arguments_rejected_before_any_device_call(lib, kw, code, needle
     assert needle in lib.tw_last_error().decode()
 
 
+def test_unfused_entries_validate(lib):
+    arr = (ctypes.c_void_p * 2)(A, A + MB)
+    assert lib.tw_reduce_partials(arr, 0, A + 12 * MB, 4, 64, 1, None) == INVALID
+    assert lib.tw_reduce_partials(arr, 2, None, 4, 64, 1, None) == INVALID
+    assert lib.tw_reduce_partials(arr, 2, A + 16, 4, 64, 1, None) == INVALID     # overlaps partial 0
+    assert b"overlaps" in lib.tw_last_error()
+    assert lib.tw_reduce_partials(arr, 2, A + 12 * MB + 8, 4, 64, 1, None) == UNSUPPORTED
+    assert lib.tw_reduce_partials(arr, 2, A + 12 * MB, 4, 12, 1, None) == UNSUPPORTED
+    assert lib.tw_reduce_partials(None, 2, None, 0, 64, 1, None) == 0           # T == 0: no-op
+    args = [A, A + 10 * MB, A + 11 * MB, A + 12 * MB, A + 13 * MB, 4, 64]
+    assert lib.tw_add_rmsnorm(*args, ctypes.c_float(-1.0), 1, None) == INVALID
+    assert lib.tw_add_rmsnorm(A, A + 10 * MB, A + 11 * MB, A, A + 13 * MB, 4, 64,
+                              ctypes.c_float(1e-5), 1, None) == INVALID          # out == input
+    assert lib.tw_add_rmsnorm(0, 0, 0, 0, 0, 0, 64, ctypes.c_float(1e-5), 1, None) == 0
+
+
 def test_shard_index_range(lib):
     for k in (-1, 2, 100):
         assert _call(lib, shard=k) == INVALID

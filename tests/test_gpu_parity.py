@@ -223,3 +223,23 @@ def test_zero_row_with_zero_eps_is_nan_documented():
     out, _ = tw.tw_fused_reduce_rmsnorm(parts, res, w, 0.0)
     torch.cuda.synchronize()
     assert torch.isnan(out[0]).all() and torch.all(out[1] == 1.0)
+
+
+# ------------------------------------------------- unfused comparator ----
+
+@pytest.mark.parametrize("name,T,h", [("tiny", 64, 512), ("llama70b", 1024, 8192),
+                                      ("mixtral", 512, 4096), ("llama70b", 7, 4104)])
+def test_unfused_comparator_matches_its_oracle(name, T, h):
+    d = make_inputs(name, num_tokens=T, hidden=h)
+    dt = d["dtype"]
+    parts, res, w = upload(d)
+    say(f"unfused {name}: T={T} h={h} {dt}")
+    out, rout, red = tw.tw_unfused_reduce_rmsnorm(parts, res, w, d["eps"])
+    torch.cuda.synchronize()
+    y, x, red_ref = oracle.unfused_reduce_rmsnorm(list(d["partials"]), d["residual"], d["weight"],
+                                                  d["eps"], dt)
+    red64 = oracle.bf16_bits_to_f64(red_ref) if dt == "bf16" else red_ref.astype(np.float64)
+    n_red = check(to_host(red), red64, dt, "reduced")
+    check(to_host(rout), x, dt, "residual_out")
+    n_y = check(to_host(out), y, dt, "out")
+    say(f"unfused {name}: reduced not bit-exact {n_red}/{red64.size}, out {n_y}/{y.size}")
