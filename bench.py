@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--no-unfused", dest="unfused", action="store_false",
                     help="skip timing the unfused comparator (standalone reduce, then a "
                          "two-pass residual-add + RMSNorm) in full mode")
+    ap.add_argument("--footprint", action="store_true",
+                    help="also sweep the fused kernel over a fixed number of workgroups "
+                         "(2 .. one per row): GB/s against the CUs the launch may occupy")
     ap.add_argument("--ceiling", action="store_true",
                     help="also time the bandwidth probes on the same buffers: N+1 streamed reads "
                          "+ 2 streamed writes, reads only, writes only (the achievable envelope; "
@@ -254,6 +257,35 @@ def main():
               f"{unfused['fused_speedup']:.3f}x", file=sys.stderr, flush=True)
         del reds
 
+    footprint = None
+    if args.footprint and args.mode == "full":
+        footprint = []
+        for G in (2, 4, 8, 16, 32, 64, 128, 256, 512, 768, T):
+            if G > T:
+                continue
+
+            def gstep(i, G=G):
+                parts, res, out, rout = sets[i % R]
+                tw.tw_fused_reduce_rmsnorm_grid(parts, res, w, wl.eps, G, out=out,
+                                                residual_out=rout, stream=stream)
+
+            k = max(5, min(args.steps, int(0.05 / max(1e-6, step_bytes / 5e12 * 256 / G))))
+            for i in range(3):
+                gstep(i)
+            torch.cuda.synchronize()
+            g0 = torch.cuda.Event(enable_timing=True)
+            g1 = torch.cuda.Event(enable_timing=True)
+            g0.record(stream)
+            for i in range(k):
+                gstep(i)
+            g1.record(stream)
+            torch.cuda.synchronize()
+            g_us = g0.elapsed_time(g1) * 1e3 / k
+            gbs_g = step_bytes / (g_us * 1e-6) / 1e9
+            footprint.append({"workgroups": G, "us": round(g_us, 2), "gbs": round(gbs_g, 1)})
+            print(f"[bench] footprint {G:5d} workgroups: {g_us:9.2f} us  {gbs_g:7.1f} GB/s",
+                  file=sys.stderr, flush=True)
+
     ceiling = None
     if args.ceiling:
         def timer(go, k):
@@ -305,6 +337,8 @@ def main():
     }
     if unfused is not None:
         result["unfused_comparator"] = unfused
+    if footprint is not None:
+        result["footprint"] = footprint
     if ceiling is not None:
         result["ceiling"] = ceiling
     if args.cpu_seconds > 0:

@@ -105,6 +105,28 @@ tw_status tw_fused_reduce_rmsnorm(const void* const* partials, int32_t num_parti
                                   tw_dtype dtype, void* stream);
 
 /*
+ * tw_fused_reduce_rmsnorm_grid -- the fused step on a fixed number of
+ * workgroups.
+ *
+ * [Blog] "Fix two", kernel sketch: each CTA of the grid takes
+ * ceil(num_tokens / grid) consecutive tokens; [Blog] "What it buys": the
+ * pages' kernel runs near-optimally on about 8 SMs and is deployed on 2-8, so
+ * that the GEMM it overlaps keeps the rest.  Workgroup b processes rows
+ * [b*ceil(T/G), min(T, (b+1)*ceil(T/G))) one after another, G =
+ * num_workgroups.  Results are bit-identical to tw_fused_reduce_rmsnorm (the
+ * per-row code is the same); only how many CUs the launch can occupy changes.
+ *
+ * Arguments are those of tw_fused_reduce_rmsnorm plus
+ *   num_workgroups  G >= 1 (else TW_ERR_INVALID_ARG); G >= T runs one
+ *                   workgroup per row, as tw_fused_reduce_rmsnorm does.
+ */
+tw_status tw_fused_reduce_rmsnorm_grid(const void* const* partials, int32_t num_partials,
+                                       const void* residual, const void* weight,
+                                       void* out, void* residual_out,
+                                       int64_t num_tokens, int64_t hidden, float eps,
+                                       tw_dtype dtype, int32_t num_workgroups, void* stream);
+
+/*
  * tw_shard_rmsnorm -- the fused step on one rank's token shard.
  *
  * [Blog] "Fix two": after a ReduceScatter split at token boundaries each of

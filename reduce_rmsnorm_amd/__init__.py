@@ -4,6 +4,8 @@ token-split planner, behind the C ABI in ``include/tokenweave.h``.
 The Python names mirror the C entry points:
 
 * :func:`tw_fused_reduce_rmsnorm` -- every row,
+* :func:`tw_fused_reduce_rmsnorm_grid` -- every row on a fixed number of
+  workgroups (the pages' few-CTA footprint),
 * :func:`tw_shard_rmsnorm` -- one rank's token shard,
 * :func:`tw_split_plan` -- the prefix/suffix split plan,
 * :func:`tw_fused_reduce_rmsnorm_split` -- the two launches of a split,
@@ -19,6 +21,7 @@ from ._lib import (  # noqa: F401
     declared_functions,
     load_library,
     tw_fused_reduce_rmsnorm,
+    tw_fused_reduce_rmsnorm_grid,
     tw_add_rmsnorm,
     tw_fused_reduce_rmsnorm_split,
     tw_reduce_partials,

@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     common = [ctypes.POINTER(vp), i32, vp, vp, vp, vp, i64, i64, ctypes.c_float, ctypes.c_int]
     lib.tw_fused_reduce_rmsnorm.argtypes = common + [vp]
     lib.tw_fused_reduce_rmsnorm.restype = ctypes.c_int
+    lib.tw_fused_reduce_rmsnorm_grid.argtypes = common + [i32, vp]
+    lib.tw_fused_reduce_rmsnorm_grid.restype = ctypes.c_int
     lib.tw_shard_rmsnorm.argtypes = common + [i32, vp]
     lib.tw_shard_rmsnorm.restype = ctypes.c_int
     lib.tw_reduce_partials.argtypes = [ctypes.POINTER(vp), i32, vp, i64, i64, ctypes.c_int, vp]
@@ -164,6 +166,24 @@ def tw_fused_reduce_rmsnorm(partials, residual: torch.Tensor, weight: torch.Tens
                                            out.data_ptr(), residual_out.data_ptr(), T, h,
                                            float(eps), _dtype_code(residual),
                                            _stream_handle(residual.device, stream)))
+    return out, residual_out
+
+
+def tw_fused_reduce_rmsnorm_grid(partials, residual: torch.Tensor, weight: torch.Tensor,
+                                 eps: float, num_workgroups: int,
+                                 out: Optional[torch.Tensor] = None,
+                                 residual_out: Optional[torch.Tensor] = None,
+                                 stream: Optional[torch.cuda.Stream] = None):
+    """The fused step on at most ``num_workgroups`` workgroups, each taking
+    ceil(T / G) consecutive rows; bit-identical to tw_fused_reduce_rmsnorm."""
+    lib = load_library()
+    parts, ptrs, T, h, out, residual_out = _marshal(partials, residual, weight, out, residual_out)
+    with torch.cuda.device(residual.device):
+        _check(lib.tw_fused_reduce_rmsnorm_grid(ptrs, len(parts), residual.data_ptr(),
+                                                weight.data_ptr(), out.data_ptr(),
+                                                residual_out.data_ptr(), T, h, float(eps),
+                                                _dtype_code(residual), int(num_workgroups),
+                                                _stream_handle(residual.device, stream)))
     return out, residual_out
 
 

@@ -127,7 +127,8 @@ tw_status validate(const void* const* partials, int32_t n, const void* residual,
 
 tw_status launch_rows(const void* const* partials, int32_t n, const void* residual,
                       const void* weight, void* out, void* residual_out, int64_t row_begin,
-                      int64_t row_end, int64_t h, float eps, tw_dtype dtype, void* stream) {
+                      int64_t row_end, int64_t h, float eps, tw_dtype dtype, void* stream,
+                      int64_t max_workgroups = 0) {
   if (row_end <= row_begin) return TW_OK;
   FusedLaunch L{};
   for (int32_t i = 0; i < n; ++i) L.partials[i] = partials[i];
@@ -142,6 +143,7 @@ tw_status launch_rows(const void* const* partials, int32_t n, const void* residu
   L.eps = eps;
   L.dtype = (int32_t)dtype;
   L.stream = stream;
+  L.max_workgroups = max_workgroups;
   char msg[256];
   if (launch_fused(L, msg, sizeof(msg)) != 0) {
     set_error("%s", msg);
@@ -166,6 +168,23 @@ tw_status tw_fused_reduce_rmsnorm(const void* const* partials, int32_t num_parti
   if (s != TW_OK || num_tokens == 0) return s;
   return tw::launch_rows(partials, num_partials, residual, weight, out, residual_out, 0,
                          num_tokens, hidden, eps, dtype, stream);
+}
+
+tw_status tw_fused_reduce_rmsnorm_grid(const void* const* partials, int32_t num_partials,
+                                       const void* residual, const void* weight, void* out,
+                                       void* residual_out, int64_t num_tokens, int64_t hidden,
+                                       float eps, tw_dtype dtype, int32_t num_workgroups,
+                                       void* stream) {
+  const tw_status s = tw::validate(partials, num_partials, residual, weight, out, residual_out,
+                                   num_tokens, hidden, eps, dtype, "tw_fused_reduce_rmsnorm_grid");
+  if (s != TW_OK) return s;
+  if (num_workgroups < 1) {
+    tw::set_error("tw_fused_reduce_rmsnorm_grid: num_workgroups=%d must be >= 1", num_workgroups);
+    return TW_ERR_INVALID_ARG;
+  }
+  if (num_tokens == 0) return TW_OK;
+  return tw::launch_rows(partials, num_partials, residual, weight, out, residual_out, 0,
+                         num_tokens, hidden, eps, dtype, stream, num_workgroups);
 }
 
 tw_status tw_shard_rmsnorm(const void* const* partials, int32_t num_partials,

@@ -65,110 +65,146 @@ struct KArgs {
   float eps;
 };
 
+// The per-row body of both fused kernels: everything the fused step does to
+// the row ROW_EXPR, by one workgroup, with the wave partial sums in the LDS
+// array wave_part[BLOCK / 64] and E, NW in scope.  Written once and expanded
+// into each kernel, so that both compile it in a kernel's own context (an
+// inlined device function allocated registers differently and spilled).
+#define TW_FUSED_ROW_BODY(ROW_EXPR)                                                    \
+  const int tid = threadIdx.x;                                                         \
+  const int64_t row = (ROW_EXPR);                                                      \
+  const int64_t base = row * (int64_t)a.nvec;                                          \
+  const int nvec = a.nvec;                                                             \
+                                                                                       \
+  int vi[VPT];                                                                         \
+  bool valid[VPT];                                                                     \
+_Pragma("unroll")                                                                      \
+  for (int j = 0; j < VPT; ++j) {                                                      \
+    const int v = tid + j * BLOCK;                                                     \
+    valid[j] = v < nvec;                                                               \
+    vi[j] = valid[j] ? v : nvec - 1;                                                   \
+  }                                                                                    \
+                                                                                       \
+  /* Loads are issued CHUNK vector slots at a time: with CHUNK == VPT every */         \
+  /* load of the row is in flight before the first use; wide rows (large VPT) */       \
+  /* take one slot's N+1 loads at a time so the row's values fit in registers. */      \
+  /* The arithmetic runs slot by slot in the same order either way. */                 \
+  constexpr int CHUNK = VPT <= 2 ? VPT : 1;                                            \
+  u32x4 wraw[VPT];                                                                     \
+  if constexpr (CHUNK == VPT) {                                                        \
+_Pragma("unroll")                                                                      \
+    for (int j = 0; j < VPT; ++j) wraw[j] = a.weight[vi[j]];                           \
+  }                                                                                    \
+                                                                                       \
+  /* Compensated float32 sum: partials in order, then the residual. */                 \
+  float x[VPT][E];                                                                     \
+  float ss = 0.0f;                                                                     \
+_Pragma("unroll")                                                                      \
+  for (int j0 = 0; j0 < VPT; j0 += CHUNK) {                                            \
+    u32x4 raw[N + 1][CHUNK];                                                           \
+_Pragma("unroll")                                                                      \
+    for (int i = 0; i < N; ++i)                                                        \
+_Pragma("unroll")                                                                      \
+      for (int jj = 0; jj < CHUNK; ++jj)                                               \
+        raw[i][jj] = __builtin_nontemporal_load(a.partials[i] + base + vi[j0 + jj]);   \
+_Pragma("unroll")                                                                      \
+    for (int jj = 0; jj < CHUNK; ++jj)                                                 \
+      raw[N][jj] = __builtin_nontemporal_load(a.residual + base + vi[j0 + jj]);        \
+_Pragma("unroll")                                                                      \
+    for (int jj = 0; jj < CHUNK; ++jj) {                                               \
+      const int j = j0 + jj;                                                           \
+      float s[E], c[E], t[E];                                                          \
+      unpack<BF16>(raw[0][jj], s);                                                     \
+_Pragma("unroll")                                                                      \
+      for (int e = 0; e < E; ++e) c[e] = 0.0f;                                         \
+_Pragma("unroll")                                                                      \
+      for (int i = 1; i <= N; ++i) {                                                   \
+        unpack<BF16>(raw[i][jj], t);                                                   \
+_Pragma("unroll")                                                                      \
+        for (int e = 0; e < E; ++e) two_sum_into(s[e], c[e], t[e]);                    \
+      }                                                                                \
+      float keep[E];                                                                   \
+_Pragma("unroll")                                                                      \
+      for (int e = 0; e < E; ++e) {                                                    \
+        const float xe = s[e] + c[e];                                                  \
+        x[j][e] = valid[j] ? xe : 0.0f;                                                \
+        keep[e] = BF16 ? round_to_odd(s[e], c[e], xe) : xe;                            \
+      }                                                                                \
+      if (valid[j])                                                                    \
+        __builtin_nontemporal_store(pack<BF16>(keep), a.residual_out + base + vi[j]);  \
+_Pragma("unroll")                                                                      \
+      for (int e = 0; e < E; ++e) ss = __builtin_fmaf(x[j][e], x[j][e], ss);           \
+    }                                                                                  \
+    if constexpr (CHUNK < VPT) __builtin_amdgcn_sched_barrier(0);                      \
+  }                                                                                    \
+  if constexpr (CHUNK < VPT) {                                                         \
+_Pragma("unroll")                                                                      \
+    for (int j = 0; j < VPT; ++j) wraw[j] = a.weight[vi[j]];                           \
+  }                                                                                    \
+                                                                                       \
+  /* Row sum of squares: wave, then waves in order through LDS. */                     \
+  const float wsum = wave_sum(ss);                                                     \
+  if ((tid & 63) == 0) wave_part[tid >> 6] = wsum;                                     \
+  __syncthreads();                                                                     \
+  float total = wave_part[0];                                                          \
+_Pragma("unroll")                                                                      \
+  for (int w = 1; w < NW; ++w) total += wave_part[w];                                  \
+  const float rs = __builtin_amdgcn_rsqf(total / a.hidden + a.eps);                    \
+                                                                                       \
+_Pragma("unroll")                                                                      \
+  for (int j = 0; j < VPT; ++j) {                                                      \
+    float w[E], y[E];                                                                  \
+    unpack<BF16>(wraw[j], w);                                                          \
+_Pragma("unroll")                                                                      \
+    for (int e = 0; e < E; ++e) y[e] = (x[j][e] * rs) * w[e];                          \
+    if (valid[j]) __builtin_nontemporal_store(pack<BF16>(y), a.out + base + vi[j]);    \
+  }
+
+// One workgroup per row: the launch grid is the row count.
 template <int N, int BLOCK, int VPT, bool BF16, int WPE>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(WPE)))
 void fused_reduce_rmsnorm_kernel(KArgs a) {
   constexpr int E = Elem<BF16>::kPerVec;
   constexpr int NW = BLOCK / 64;
   __shared__ float wave_part[NW];
+  TW_FUSED_ROW_BODY(a.row_begin + blockIdx.x)
+}
 
-  const int tid = threadIdx.x;
-  const int64_t row = a.row_begin + blockIdx.x;
-  const int64_t base = row * (int64_t)a.nvec;
-  const int nvec = a.nvec;
-
-  int vi[VPT];
-  bool valid[VPT];
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    const int v = tid + j * BLOCK;
-    valid[j] = v < nvec;
-    vi[j] = valid[j] ? v : nvec - 1;
-  }
-
-  // Loads are issued CHUNK vector slots at a time: with CHUNK == VPT every
-  // load of the row is in flight before the first use; wide rows (large VPT)
-  // take one slot's N+1 loads at a time so the row's values fit in registers.
-  // The arithmetic runs slot by slot in the same order either way.
-  constexpr int CHUNK = VPT <= 2 ? VPT : 1;
-  u32x4 wraw[VPT];
-  if constexpr (CHUNK == VPT) {
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) wraw[j] = a.weight[vi[j]];
-  }
-
-  // Compensated float32 sum: partials in order, then the residual.
-  float x[VPT][E];
-  float ss = 0.0f;
-#pragma unroll
-  for (int j0 = 0; j0 < VPT; j0 += CHUNK) {
-    u32x4 raw[N + 1][CHUNK];
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-#pragma unroll
-      for (int jj = 0; jj < CHUNK; ++jj)
-        raw[i][jj] = __builtin_nontemporal_load(a.partials[i] + base + vi[j0 + jj]);
-#pragma unroll
-    for (int jj = 0; jj < CHUNK; ++jj)
-      raw[N][jj] = __builtin_nontemporal_load(a.residual + base + vi[j0 + jj]);
-#pragma unroll
-    for (int jj = 0; jj < CHUNK; ++jj) {
-      const int j = j0 + jj;
-      float s[E], c[E], t[E];
-      unpack<BF16>(raw[0][jj], s);
-#pragma unroll
-      for (int e = 0; e < E; ++e) c[e] = 0.0f;
-#pragma unroll
-      for (int i = 1; i <= N; ++i) {
-        unpack<BF16>(raw[i][jj], t);
-#pragma unroll
-        for (int e = 0; e < E; ++e) two_sum_into(s[e], c[e], t[e]);
-      }
-      float keep[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float xe = s[e] + c[e];
-        x[j][e] = valid[j] ? xe : 0.0f;
-        keep[e] = BF16 ? round_to_odd(s[e], c[e], xe) : xe;
-      }
-      if (valid[j])
-        __builtin_nontemporal_store(pack<BF16>(keep), a.residual_out + base + vi[j]);
-#pragma unroll
-      for (int e = 0; e < E; ++e) ss = __builtin_fmaf(x[j][e], x[j][e], ss);
-    }
-    if constexpr (CHUNK < VPT) __builtin_amdgcn_sched_barrier(0);
-  }
-  if constexpr (CHUNK < VPT) {
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) wraw[j] = a.weight[vi[j]];
-  }
-
-  // Row sum of squares: wave, then waves in order through LDS.
-  const float wsum = wave_sum(ss);
-  if ((tid & 63) == 0) wave_part[tid >> 6] = wsum;
-  __syncthreads();
-  float total = wave_part[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) total += wave_part[w];
-  const float rs = __builtin_amdgcn_rsqf(total / a.hidden + a.eps);
-
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    float w[E], y[E];
-    unpack<BF16>(wraw[j], w);
-#pragma unroll
-    for (int e = 0; e < E; ++e) y[e] = (x[j][e] * rs) * w[e];
-    if (valid[j]) __builtin_nontemporal_store(pack<BF16>(y), a.out + base + vi[j]);
+// A fixed number of workgroups: workgroup b takes the consecutive rows
+// [b*rows_per_wg, min((b+1)*rows_per_wg, row_end)), as the blog's kernel
+// sketch partitions tokens over its CTAs (tokens per CTA = ceil(T / grid)).
+// A barrier between rows keeps a row's wave partial sums from overwriting the
+// previous row's while a slower wave still reads them.  Few workgroups are
+// launched by design, so no occupancy cap is requested.
+template <int N, int BLOCK, int VPT, bool BF16>
+__global__ __launch_bounds__(BLOCK) void fused_reduce_rmsnorm_rows_kernel(KArgs a,
+                                                                          int64_t rows_per_wg,
+                                                                          int64_t row_end) {
+  constexpr int E = Elem<BF16>::kPerVec;
+  constexpr int NW = BLOCK / 64;
+  __shared__ float wave_part[NW];
+  const int64_t first = a.row_begin + (int64_t)blockIdx.x * rows_per_wg;
+  const int64_t last = first + rows_per_wg < row_end ? first + rows_per_wg : row_end;
+  for (int64_t r = first; r < last; ++r) {
+    if (r != first) __syncthreads();
+    TW_FUSED_ROW_BODY(r)
   }
 }
 
 using KernelFn = void (*)(KArgs);
+using RowsKernelFn = void (*)(KArgs, int64_t, int64_t);
+
+template <int N, int G> constexpr int kWavesPerEu =
+    N <= kMaxCappedPartials ? kGeometry[G].waves_per_eu : 1;
 
 template <bool BF16, int G, int... Ns>
 constexpr std::array<KernelFn, sizeof...(Ns)> row_of(std::integer_sequence<int, Ns...>) {
   return {&fused_reduce_rmsnorm_kernel<Ns + 1, kGeometry[G].block, kGeometry[G].vpt, BF16,
-                                       (Ns + 1 <= kMaxCappedPartials ? kGeometry[G].waves_per_eu
-                                                                     : 1)>...};
+                                       kWavesPerEu<Ns + 1, G>>...};
+}
+template <bool BF16, int G, int... Ns>
+constexpr std::array<RowsKernelFn, sizeof...(Ns)> rows_row_of(std::integer_sequence<int, Ns...>) {
+  return {&fused_reduce_rmsnorm_rows_kernel<Ns + 1, kGeometry[G].block, kGeometry[G].vpt, BF16>...};
 }
 
 template <bool BF16, int... Gs>
@@ -176,9 +212,16 @@ constexpr std::array<std::array<KernelFn, kMaxPartials>, sizeof...(Gs)> table_of
     std::integer_sequence<int, Gs...>) {
   return {row_of<BF16, Gs>(std::make_integer_sequence<int, kMaxPartials>{})...};
 }
+template <bool BF16, int... Gs>
+constexpr std::array<std::array<RowsKernelFn, kMaxPartials>, sizeof...(Gs)> rows_table_of(
+    std::integer_sequence<int, Gs...>) {
+  return {rows_row_of<BF16, Gs>(std::make_integer_sequence<int, kMaxPartials>{})...};
+}
 
 const auto kTableF32 = table_of<false>(std::make_integer_sequence<int, kNumGeometries>{});
 const auto kTableBF16 = table_of<true>(std::make_integer_sequence<int, kNumGeometries>{});
+const auto kRowsTableF32 = rows_table_of<false>(std::make_integer_sequence<int, kNumGeometries>{});
+const auto kRowsTableBF16 = rows_table_of<true>(std::make_integer_sequence<int, kNumGeometries>{});
 
 }  // namespace
 
@@ -210,11 +253,22 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
   k.hidden = (float)L.hidden;
   k.eps = L.eps;
 
-  const KernelFn fn = bf16 ? kTableBF16[g][L.num_partials - 1] : kTableF32[g][L.num_partials - 1];
-  void* args[] = {&k};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn),
-                                       dim3((unsigned)L.num_rows), dim3(kGeometry[g].block), args, 0,
-                                       static_cast<hipStream_t>(L.stream));
+  hipError_t e;
+  if (L.max_workgroups <= 0 || L.max_workgroups >= L.num_rows) {
+    const KernelFn fn = bf16 ? kTableBF16[g][L.num_partials - 1] : kTableF32[g][L.num_partials - 1];
+    void* args[] = {&k};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)L.num_rows),
+                        dim3(kGeometry[g].block), args, 0, static_cast<hipStream_t>(L.stream));
+  } else {
+    const RowsKernelFn fn =
+        bf16 ? kRowsTableBF16[g][L.num_partials - 1] : kRowsTableF32[g][L.num_partials - 1];
+    int64_t rows_per_wg = (L.num_rows + L.max_workgroups - 1) / L.max_workgroups;
+    int64_t row_end = L.row_begin + L.num_rows;
+    const unsigned grid = (unsigned)((L.num_rows + rows_per_wg - 1) / rows_per_wg);
+    void* args[] = {&k, &rows_per_wg, &row_end};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(kGeometry[g].block),
+                        args, 0, static_cast<hipStream_t>(L.stream));
+  }
   if (e != hipSuccess) {
     std::snprintf(err, errlen, "hipLaunchKernel: %s", hipGetErrorString(e));
     return (int)e;

@@ -22,6 +22,7 @@ struct FusedLaunch {
   float eps;
   int32_t dtype;       // tw_dtype value
   void* stream;        // hipStream_t
+  int64_t max_workgroups;   // <= 0: one workgroup per row; else at most this many
 };
 
 // Enqueues the kernel.  Returns 0 on success; otherwise writes a message to

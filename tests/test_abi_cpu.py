@@ -36,6 +36,13 @@ def test_exports_every_declared_symbol(lib):
     assert lib.tw_abi_version() == 1
 
 
+def test_every_entry_point_has_a_python_binding():
+    support = {"tw_status_string", "tw_last_error", "tw_abi_version"}
+    for n in tw.declared_functions():
+        if n not in support:
+            assert callable(getattr(tw, n, None)), f"reduce_rmsnorm_amd.{n} missing"
+
+
 def test_status_strings(lib):
     for s in range(4):
         assert lib.tw_status_string(s).startswith(b"TW_")
@@ -112,6 +119,18 @@ def test_unfused_entries_validate(lib):
     assert lib.tw_add_rmsnorm(A, A + 10 * MB, A + 11 * MB, A, A + 13 * MB, 4, 64,
                               ctypes.c_float(1e-5), 1, None) == INVALID          # out == input
     assert lib.tw_add_rmsnorm(0, 0, 0, 0, 0, 0, 64, ctypes.c_float(1e-5), 1, None) == 0
+
+
+def test_grid_entry_validates_workgroups(lib):
+    parts = (ctypes.c_void_p * 2)(A, A + MB)
+    args = [parts, 2, A + 10 * MB, A + 11 * MB, A + 12 * MB, A + 13 * MB, 4, 64,
+            ctypes.c_float(1e-5), 1]
+    for g in (0, -3):
+        assert lib.tw_fused_reduce_rmsnorm_grid(*args, g, None) == INVALID
+        assert b"num_workgroups" in lib.tw_last_error()
+    bad = list(args)
+    bad[8] = ctypes.c_float(-1.0)
+    assert lib.tw_fused_reduce_rmsnorm_grid(*bad, 8, None) == INVALID
 
 
 def test_shard_index_range(lib):

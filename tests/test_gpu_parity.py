@@ -243,3 +243,21 @@ def test_unfused_comparator_matches_its_oracle(name, T, h):
     check(to_host(rout), x, dt, "residual_out")
     n_y = check(to_host(out), y, dt, "out")
     say(f"unfused {name}: reduced not bit-exact {n_red}/{red64.size}, out {n_y}/{y.size}")
+
+
+# --------------------------------------------- fixed number of workgroups ----
+
+@pytest.mark.parametrize("name,T,h", [("llama70b", 1024, 8192), ("tiny", 64, 512), ("mixtral", 333, 4096)])
+def test_grid_launch_bit_identical_to_one_row_per_workgroup(name, T, h):
+    d = make_inputs(name, num_tokens=T, hidden=h)
+    parts, res, w = upload(d)
+    say(f"grid reference {name}: T={T} h={h}")
+    out_ref, rout_ref = _run_full(parts, res, w, d["eps"])
+    for G in (1, 2, 3, 8, 100, 256, T - 1, T, T + 5):
+        if G < 1:
+            continue
+        say(f"grid {name}: {G} workgroups")
+        out, rout = tw.tw_fused_reduce_rmsnorm_grid(parts, res, w, d["eps"], G)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_host(out), out_ref)
+        np.testing.assert_array_equal(to_host(rout), rout_ref)
