@@ -65,6 +65,10 @@ def parse():
     ap.add_argument("--footprint", action="store_true",
                     help="also sweep the fused kernel over a fixed number of workgroups "
                          "(2 .. one per row): GB/s against the CUs the launch may occupy")
+    ap.add_argument("--overlap", action="store_true",
+                    help="also time one tensor-parallel layer step (row-parallel GEMM + fused "
+                         "step) unsplit and split in two on two streams, for every offset, at "
+                         "several token counts: the measured offset sweep")
     ap.add_argument("--ceiling", action="store_true",
                     help="also time the bandwidth probes on the same buffers: N+1 streamed reads "
                          "+ 2 streamed writes, reads only, writes only (the achievable envelope; "
@@ -107,6 +111,87 @@ def run_ceiling(sets, R, rows, h, itemsize, stream, steps, timer):
         print(f"[bench] probe {key}: {nbytes} B in {us:.2f} us = {res[key + '_gbs']} GB/s",
               file=sys.stderr, flush=True)
     return res
+
+
+# Down-projection of a Llama-3-70B-shaped layer under 8-way tensor
+# parallelism: intermediate 28672 / 8 = 3584 columns per rank.
+OVERLAP_K = 3584
+
+
+def _on(stream, fn, i):
+    import torch
+    with torch.cuda.stream(stream):
+        fn(i)
+
+
+def run_overlap(tw, torch, wl, plan_kw) -> list:
+    """For each token count: the unsplit step and every feasible split offset,
+    each captured as a HIP graph per rotated buffer set and replayed (no host
+    launch cost), plus the eager (Python-launched) times for reference."""
+    from reduce_rmsnorm_amd.overlap import LayerStep, capture, time_graphs, time_steps
+    # Two side streams, default priority (graphs are captured off the null stream).
+    stream_a = torch.cuda.Stream()
+    stream_b = torch.cuda.Stream()
+    rows = []
+    for T in (1024, 2048, 4096, 8192):
+        step = LayerStep(T, wl.hidden, OVERLAP_K, wl.num_partials, eps=wl.eps, sets=2)
+        iters = max(20, int(4e-3 / (T * 4e-9 + 1e-6)))
+
+        def measure(fn):
+            # Eager first: it also lets the GEMM library finish its lazy per-shape
+            # set-up, which it may not do while a stream is being captured.
+            e_us = time_steps(fn, stream_a, stream_b, max(10, iters // 4))
+            graphs = [capture(fn, stream_a, stream_b, i) for i in range(2)]
+            g_us = time_graphs(graphs, stream_a, iters)
+            del graphs
+            return g_us, e_us
+
+        base, base_e = measure(lambda i: step.run_unsplit(i, stream_a))
+        plan = tw.tw_split_plan(T, **plan_kw)
+        entry = {"tokens": T, "unsplit_us": round(base, 2), "unsplit_eager_us": round(base_e, 2),
+                 "planner": plan, "splits": []}
+        half = T // 2
+        for off in (0, 64, 128, 192, 256, 512):
+            if off >= half:
+                continue
+            us, us_e = measure(lambda i, p=half + off: step.run_split(i, p, stream_a, stream_b))
+            entry["splits"].append({"offset": off, "prefix": half + off, "us": round(us, 2),
+                                    "eager_us": round(us_e, 2), "speedup": round(base / us, 4)})
+        best = min(entry["splits"], key=lambda e: e["us"])
+        entry["best_offset"] = best["offset"]
+        entry["best_speedup"] = best["speedup"]
+        # The fused kernel confined to G workgroups during the overlap (the
+        # pages run theirs on a few SMs so the GEMM keeps the rest).
+        entry["splits_workgroups"] = []
+        for G in (64, 128, 256):
+            us, _ = measure(lambda i, p=half + best["offset"], G=G:
+                            step.run_split(i, p, stream_a, stream_b, workgroups=G))
+            entry["splits_workgroups"].append({"workgroups": G, "offset": best["offset"],
+                                               "us": round(us, 2)})
+        # Components alone (graph replays, one stream).
+        comp = {}
+        for name, lo, hi, kind in (("gemm_all", 0, T, "g"), ("gemm_half", 0, half, "g"),
+                                   ("fused_all", 0, T, "f"), ("fused_half", 0, half, "f")):
+            if kind == "g":
+                fn = (lambda i, lo=lo, hi=hi: step._gemm(i, lo, hi))
+            else:
+                fn = (lambda i, lo=lo, hi=hi: step._fused(i, lo, hi, torch.cuda.current_stream(),
+                                                          None))
+            comp[name], _ = measure(lambda i, fn=fn: _on(stream_a, fn, i))
+            comp[name] = round(comp[name], 2)
+        entry["components_us"] = comp
+        rows.append(entry)
+        print(f"[bench] overlap T={T} (graph replay): unsplit {base:.1f} us; " + ", ".join(
+            f"off {e['offset']}: {e['us']:.1f}" for e in entry["splits"]) +
+            f"; best off {best['offset']} ({best['speedup']:.3f}x); planner reason "
+            f"{plan['reason']} off {plan['offset']}; eager unsplit {base_e:.1f} us, eager "
+            f"splits " + ", ".join(f"{e['eager_us']:.1f}" for e in entry["splits"]) +
+            "; confined fused: " + ", ".join(f"G={e['workgroups']}: {e['us']:.1f}"
+                                             for e in entry["splits_workgroups"]) +
+            f"; components {entry['components_us']}", file=sys.stderr, flush=True)
+        del step
+        torch.cuda.empty_cache()
+    return rows
 
 
 def cpu_baseline(wl, d, budget_s: float) -> dict:
@@ -286,6 +371,10 @@ def main():
             print(f"[bench] footprint {G:5d} workgroups: {g_us:9.2f} us  {gbs_g:7.1f} GB/s",
                   file=sys.stderr, flush=True)
 
+    overlap = None
+    if args.overlap:
+        overlap = run_overlap(tw, torch, wl, plan_kw)
+
     ceiling = None
     if args.ceiling:
         def timer(go, k):
@@ -339,6 +428,8 @@ def main():
         result["unfused_comparator"] = unfused
     if footprint is not None:
         result["footprint"] = footprint
+    if overlap is not None:
+        result["overlap"] = overlap
     if ceiling is not None:
         result["ceiling"] = ceiling
     if args.cpu_seconds > 0:

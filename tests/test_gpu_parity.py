@@ -261,3 +261,61 @@ def test_grid_launch_bit_identical_to_one_row_per_workgroup(name, T, h):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(to_host(out), out_ref)
         np.testing.assert_array_equal(to_host(rout), rout_ref)
+
+
+# ------------------------------------------------ overlapped layer step ----
+
+def test_overlapped_split_step_equals_one_fused_launch():
+    from reduce_rmsnorm_amd.overlap import LayerStep
+    T, h, K, N = 300, 1024, 256, 4
+    step = LayerStep(T, h, K, N, eps=1e-5, sets=1, seed=3)
+    a, b = torch.cuda.current_stream(), torch.cuda.Stream()
+    for prefix in (150, 214, 299, 1):
+        say(f"overlapped split step T={T} prefix={prefix}")
+        step.run_split(0, prefix, a, b)
+        a.wait_stream(b)
+        torch.cuda.synchronize()
+        parts, res, out, rout = step.outputs(0)
+        out_s, rout_s = to_host(out), to_host(rout)
+        # the same partials (P_0 now holds the GEMM rows) through one launch
+        ref_out, ref_rout = _run_full(parts, res, step.weight, 1e-5)
+        np.testing.assert_array_equal(out_s, ref_out)
+        np.testing.assert_array_equal(rout_s, ref_rout)
+    p_host = to_host(parts)
+    y, x, _ = oracle.fused_reduce_rmsnorm(list(p_host), to_host(res), to_host(step.weight), 1e-5, "bf16")
+    check(out_s, y, "bf16", "out")
+    check(rout_s, x, "bf16", "residual_out")
+    say("overlapped unsplit step")
+    step.run_unsplit(0, a)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(step.outputs(0)[2]), _run_full(parts, res, step.weight, 1e-5)[0])
+
+
+def test_captured_split_step_replays_match_eager():
+    # Graph replays, with eager work and synchronizations between them, must
+    # each reproduce the eager step's outputs.
+    from reduce_rmsnorm_amd.overlap import LayerStep, capture
+    T, h, K, N = 512, 1024, 256, 8
+    step = LayerStep(T, h, K, N, eps=1e-5, sets=1, seed=4)
+    a, b = torch.cuda.Stream(), torch.cuda.Stream()
+    say("eager split step (reference)")
+    step.run_split(0, 320, a, b)
+    a.wait_stream(b)
+    torch.cuda.synchronize()
+    ref = [to_host(t) for t in step.outputs(0)]
+    say("capture split step")
+    g = capture(lambda i: step.run_split(i, 320, a, b), a, b, 0)
+    for rep in range(4):
+        parts, res, out, rout = step.outputs(0)
+        out.fill_(0)
+        rout.fill_(0)
+        parts[0].fill_(0)
+        torch.cuda.synchronize()
+        say(f"replay {rep}")
+        with torch.cuda.stream(a):
+            g.replay()
+        torch.cuda.synchronize()
+        got = [to_host(t) for t in step.outputs(0)]
+        for x, y in zip(got, ref):
+            np.testing.assert_array_equal(x, y)
+        _ = torch.ones(1000, device="cuda").sum().item()      # eager work between replays
