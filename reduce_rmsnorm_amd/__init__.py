@@ -12,11 +12,16 @@ The Python names mirror the C entry points:
 * :func:`tw_reduce_partials`, :func:`tw_add_rmsnorm` and
   :func:`tw_unfused_reduce_rmsnorm` -- the unfused comparator (a standalone
   reduction, then a standard two-pass residual-add + RMSNorm).
+
+:class:`PreparedFused` marshals a launch once for loops that repeat it, and
+:class:`SplitPlanCache` keeps one split plan per token count.
 """
 
 from ._lib import (  # noqa: F401
     LIB_PATH,
     PLAN_REASONS,
+    PreparedFused,
+    SplitPlanCache,
     TokenWeaveError,
     declared_functions,
     load_library,

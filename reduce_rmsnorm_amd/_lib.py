@@ -287,3 +287,53 @@ def tw_fused_reduce_rmsnorm_split(partials, residual: torch.Tensor, weight: torc
         tw_fused_reduce_rmsnorm([p[lo:hi] for p in parts], residual[lo:hi], weight, eps,
                                 out=out[lo:hi], residual_out=residual_out[lo:hi], stream=stream)
     return out, residual_out
+
+
+class PreparedFused:
+    """A fused launch with its arguments marshalled once.
+
+    For loops that launch the same step on the same buffers (a serving loop, a
+    benchmark): the tensors are checked and turned into pointers here, each
+    call is then one C call on the given stream.  The C side still validates
+    every call.  ``mode`` is "full", "shard" (needs ``shard_index``) or "grid"
+    (needs ``num_workgroups``).  Keeps references to every tensor it uses.
+    """
+
+    def __init__(self, partials, residual, weight, eps: float, out: torch.Tensor,
+                 residual_out: torch.Tensor, stream: Optional[torch.cuda.Stream] = None,
+                 mode: str = "full", shard_index: int = 0, num_workgroups: int = 0):
+        lib = load_library()
+        parts, ptrs, T, h, out, residual_out = _marshal(partials, residual, weight, out,
+                                                        residual_out)
+        self._keep = (parts, residual, weight, out, residual_out, ptrs)
+        self.out, self.residual_out = out, residual_out
+        head = (ptrs, len(parts), residual.data_ptr(), weight.data_ptr(), out.data_ptr(),
+                residual_out.data_ptr(), T, h, ctypes.c_float(float(eps)), _dtype_code(residual))
+        s = _stream_handle(residual.device, stream)
+        if mode == "full":
+            self._fn, self._args = lib.tw_fused_reduce_rmsnorm, head + (s,)
+        elif mode == "shard":
+            self._fn, self._args = lib.tw_shard_rmsnorm, head + (int(shard_index), s)
+        elif mode == "grid":
+            self._fn, self._args = lib.tw_fused_reduce_rmsnorm_grid, head + (int(num_workgroups), s)
+        else:
+            raise ValueError(f"unknown mode {mode!r}")
+
+    def __call__(self) -> None:
+        _check(self._fn(*self._args))
+
+
+class SplitPlanCache:
+    """Split plans by token count for one model/GEMM configuration: each
+    count is planned once by tw_split_plan and then looked up, as the pages
+    keep the chosen split of each shape in a table."""
+
+    def __init__(self, **problem):
+        self._problem = problem
+        self._plans = {}
+
+    def __call__(self, num_tokens: int) -> dict:
+        plan = self._plans.get(num_tokens)
+        if plan is None:
+            plan = self._plans[num_tokens] = tw_split_plan(num_tokens, **self._problem)
+        return plan

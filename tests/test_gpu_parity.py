@@ -319,3 +319,26 @@ def test_captured_split_step_replays_match_eager():
         for x, y in zip(got, ref):
             np.testing.assert_array_equal(x, y)
         _ = torch.ones(1000, device="cuda").sum().item()      # eager work between replays
+
+
+def test_prepared_launches_match_direct_calls():
+    d = make_inputs("llama70b", num_tokens=96, hidden=8192)
+    parts, res, w = upload(d)
+    ref_out, ref_rout = _run_full(parts, res, w, d["eps"])
+    for mode, kw in (("full", {}), ("grid", {"num_workgroups": 7}), ("shard", {"shard_index": 3})):
+        out = torch.full_like(res, float("nan"))
+        rout = torch.full_like(res, float("nan"))
+        say(f"prepared launch, mode {mode}")
+        launch = tw.PreparedFused(parts, res, w, d["eps"], out, rout, mode=mode, **kw)
+        launch()
+        launch()
+        torch.cuda.synchronize()
+        rows = oracle.shard_rows(96, 8, 3) if mode == "shard" else range(96)
+        sl = slice(rows.start, rows.stop)
+        np.testing.assert_array_equal(to_host(out)[sl], ref_out[sl])
+        np.testing.assert_array_equal(to_host(rout)[sl], ref_rout[sl])
+    cache = tw.SplitPlanCache(tokens_per_cta=256, ctas_per_token_tile=32, num_cus=256,
+                              min_split_tokens=1024)
+    assert cache(4096) == oracle.split_plan(4096, tokens_per_cta=256, ctas_per_token_tile=32,
+                                            num_cus=256, min_split_tokens=1024)
+    assert cache(4096) is cache(4096)
