@@ -87,9 +87,8 @@ _Pragma("unroll")                                                               
                                                                                        \
   /* Loads are issued CHUNK vector slots at a time: with CHUNK == VPT every */         \
   /* load of the row is in flight before the first use; wide rows (large VPT) */       \
-  /* take one slot's N+1 loads at a time so the row's values fit in registers. */      \
-  /* The arithmetic runs slot by slot in the same order either way. */                 \
-  constexpr int CHUNK = VPT <= 2 ? VPT : 1;                                            \
+  /* take CHUNK slots' N+1 loads at a time so the row's values fit in */               \
+  /* registers.  The arithmetic runs slot by slot in the same order either way. */     \
   u32x4 wraw[VPT];                                                                     \
   if constexpr (CHUNK == VPT) {                                                        \
 _Pragma("unroll")                                                                      \
@@ -161,7 +160,7 @@ _Pragma("unroll")                                                               
   }
 
 // One workgroup per row: the launch grid is the row count.
-template <int N, int BLOCK, int VPT, bool BF16, int WPE>
+template <int N, int BLOCK, int VPT, bool BF16, int WPE, int CHUNK>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(WPE)))
 void fused_reduce_rmsnorm_kernel(KArgs a) {
   constexpr int E = Elem<BF16>::kPerVec;
@@ -176,7 +175,7 @@ void fused_reduce_rmsnorm_kernel(KArgs a) {
 // A barrier between rows keeps a row's wave partial sums from overwriting the
 // previous row's while a slower wave still reads them.  Few workgroups are
 // launched by design, so no occupancy cap is requested.
-template <int N, int BLOCK, int VPT, bool BF16>
+template <int N, int BLOCK, int VPT, bool BF16, int CHUNK>
 __global__ __launch_bounds__(BLOCK) void fused_reduce_rmsnorm_rows_kernel(KArgs a,
                                                                           int64_t rows_per_wg,
                                                                           int64_t row_end) {
@@ -200,11 +199,12 @@ template <int N, int G> constexpr int kWavesPerEu =
 template <bool BF16, int G, int... Ns>
 constexpr std::array<KernelFn, sizeof...(Ns)> row_of(std::integer_sequence<int, Ns...>) {
   return {&fused_reduce_rmsnorm_kernel<Ns + 1, kGeometry[G].block, kGeometry[G].vpt, BF16,
-                                       kWavesPerEu<Ns + 1, G>>...};
+                                       kWavesPerEu<Ns + 1, G>, kGeometry[G].chunk>...};
 }
 template <bool BF16, int G, int... Ns>
 constexpr std::array<RowsKernelFn, sizeof...(Ns)> rows_row_of(std::integer_sequence<int, Ns...>) {
-  return {&fused_reduce_rmsnorm_rows_kernel<Ns + 1, kGeometry[G].block, kGeometry[G].vpt, BF16>...};
+  return {&fused_reduce_rmsnorm_rows_kernel<Ns + 1, kGeometry[G].block, kGeometry[G].vpt, BF16,
+                                            kGeometry[G].chunk>...};
 }
 
 template <bool BF16, int... Gs>

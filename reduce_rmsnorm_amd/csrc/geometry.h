@@ -12,21 +12,24 @@ struct Geometry {
   int block;          // threads per workgroup
   int vpt;            // 16-byte vectors per thread
   int waves_per_eu;   // occupancy the compiler must allow (1: no constraint)
+  int chunk;          // vector slots whose loads are issued together (divides vpt)
 };
 
 // (threads per workgroup, vectors per thread) by 16-byte vectors per row: the
 // first entry whose capacity covers the row.  Measured on MI355X at 184-738 MB
-// per launch (h = 8192 bf16 has 1024 vectors): 512 x 2 beat 256 x 4 and
-// 1024 x 1; at h = 4096 512 x 1, at h = 16384 1024 x 2.  The occupancy entry
-// lets more rows be resident per CU: 512 x 2 at 6 waves per SIMD (at most 80
-// VGPRs, three workgroups per CU instead of two) took 31.6-31.9 us against
-// 32.6-32.8 us at T = 1024; 1024 x 2 at 5 waves per SIMD 132 us against
-// 137 us at h = 16384; 512 x 1 at 8 waves per SIMD 122.9 us against 123.7 us
-// at h = 4096.  The cap applies up to N = 8 partials, where it costs no
-// scratch; with more partials the compiler's own allocation is kept.
+// per launch, N = 8 bf16:
+//  * h = 8192 (1024 vectors): 512 x 2 at 6 waves per SIMD (at most 80 VGPRs,
+//    three workgroups per CU) 31.5 us; uncapped 32.7 us; 1024 x 1 33.4 us;
+//    256 x 4 36.0-36.5 us.
+//  * h = 4096 (512 vectors): 512 x 1 at 8 waves per SIMD 122.9-123.2 us
+//    (T = 8192); 256 x 2 128.9 us.
+//  * h = 16384 (2048 vectors): 512 x 4 at 4 waves per SIMD, loads two slots
+//    at a time, 123.9 us (T = 2048); 1024 x 2 133.4 us; 256 x 8 132.1 us.
+// The occupancy cap applies up to N = 8 partials, where it costs no scratch;
+// with more partials the compiler's own allocation is kept.
 constexpr Geometry kGeometry[] = {
-    {64, 1, 1},  {128, 1, 1},  {256, 1, 1},  {512, 1, 8},
-    {512, 2, 6}, {1024, 2, 5}, {1024, 4, 1}, {1024, 8, 1}};
+    {64, 1, 1, 1},  {128, 1, 1, 1}, {256, 1, 1, 1},  {512, 1, 8, 1},
+    {512, 2, 6, 2}, {512, 4, 4, 2}, {1024, 4, 1, 1}, {1024, 8, 1, 1}};
 constexpr int kMaxCappedPartials = 8;
 constexpr int kNumGeometries = sizeof(kGeometry) / sizeof(kGeometry[0]);
 constexpr int kMaxVectors = 8192;
