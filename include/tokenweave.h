@@ -21,8 +21,9 @@
  *     and the call returns after the enqueue.
  *   - Device faults surface at the caller's next synchronization; launch
  *     errors come back as TW_ERR_DEVICE.
- *   - The only global state is a thread-local last-error string, so calls
- *     from several host threads are safe.
+ *   - The only global state is a thread-local last-error string and the
+ *     process-wide pointer-check switch (an atomic), so calls from several
+ *     host threads are safe.
  *
  * Errors: every argument is checked before any HIP call is made, so an
  * argument error never touches the device.
@@ -57,6 +58,19 @@ typedef enum {
 
 /* Version of this ABI (TW_ABI_VERSION of the built library). */
 int32_t tw_abi_version(void);
+
+/*
+ * tw_set_pointer_checks -- opt-in verification of tensor pointers (default:
+ * off).  When enabled, every entry that launches a kernel also asks the HIP
+ * runtime, after the argument checks, whether each tensor is device (or
+ * managed) memory and whether its whole byte range lies inside one
+ * allocation; if not, the call returns TW_ERR_INVALID_ARG and launches
+ * nothing.  This turns a host pointer or a short buffer into an error instead
+ * of a device memory fault, for a few runtime queries per call.  The setting
+ * is process-wide and may be changed from any thread.
+ *   enabled   nonzero: on; 0: off
+ */
+void tw_set_pointer_checks(int32_t enabled);
 
 /*
  * tw_fused_reduce_rmsnorm -- the fused step for every token row.

@@ -30,6 +30,7 @@ from ._lib import (  # noqa: F401
     tw_add_rmsnorm,
     tw_fused_reduce_rmsnorm_split,
     tw_reduce_partials,
+    tw_set_pointer_checks,
     tw_shard_rmsnorm,
     tw_split_plan,
     tw_unfused_reduce_rmsnorm,

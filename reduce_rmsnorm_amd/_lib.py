@@ -83,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tw_last_error.restype = ctypes.c_char_p
     lib.tw_abi_version.argtypes = []
     lib.tw_abi_version.restype = ctypes.c_int32
+    lib.tw_set_pointer_checks.argtypes = [i32]
+    lib.tw_set_pointer_checks.restype = None
     _lib = lib
     return lib
 
@@ -92,6 +94,11 @@ def declared_functions(header: str = HEADER_PATH):
     text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(tw_[a-z0-9_]+)\s*\(", text)))
+
+
+def tw_set_pointer_checks(enabled: bool) -> None:
+    """Turn the library's opt-in device-pointer verification on or off."""
+    load_library().tw_set_pointer_checks(1 if enabled else 0)
 
 
 def _check(status: int) -> None:

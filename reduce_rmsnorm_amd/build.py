@@ -28,7 +28,9 @@ ARCH = "gfx950"
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-command-line-argument"]
-CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+# Host C++ uses the HIP runtime API only (pointer queries), through its C headers.
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+             "-I/opt/rocm/include"]
 
 HOST_SOURCES = ["api.cpp", "split_plan.cpp"]
 HIP_SOURCES = ["fused_reduce_rmsnorm.hip", "unfused.hip"]

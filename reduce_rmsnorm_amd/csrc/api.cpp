@@ -1,10 +1,13 @@
 // C ABI entry points: argument validation (before any HIP call), shard row
 // ranges, and the hand-off to the kernel launcher.  Host-only C++.
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+
+#include <hip/hip_runtime_api.h>
 
 #include "launch.h"
 #include "tokenweave.h"
@@ -23,6 +26,39 @@ void set_error(const char* fmt, ...) {
 }
 
 namespace {
+
+std::atomic<int> g_pointer_checks{0};
+
+// With pointer checks on: is [p, p + bytes) device memory inside one
+// allocation?  Uses runtime queries only (no launch); clears the runtime's
+// last error when a query fails.
+bool device_range_ok(const void* p, uint64_t bytes, const char* what, const char* who) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    set_error("%s: %s is not memory the HIP runtime knows", who, what);
+    return false;
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) {
+    set_error("%s: %s is not device memory", who, what);
+    return false;
+  }
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+    (void)hipGetLastError();
+    set_error("%s: no allocation found for %s", who, what);
+    return false;
+  }
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(base);
+  const uintptr_t ptr = reinterpret_cast<uintptr_t>(p);
+  if (ptr < lo || ptr + bytes > lo + size) {
+    set_error("%s: %s spans %llu bytes past its allocation", who, what,
+              (unsigned long long)(ptr + bytes > lo + size ? ptr + bytes - (lo + size) : 0));
+    return false;
+  }
+  return true;
+}
 
 struct Range {
   uintptr_t lo, hi;   // [lo, hi)
@@ -122,6 +158,18 @@ tw_status validate(const void* const* partials, int32_t n, const void* residual,
       return TW_ERR_INVALID_ARG;
     }
   }
+  if (g_pointer_checks.load(std::memory_order_relaxed)) {
+    char what[32];
+    for (int32_t i = 0; i < n; ++i) {
+      std::snprintf(what, sizeof(what), "partials[%d]", i);
+      if (!device_range_ok(partials[i], tensor_bytes, what, who)) return TW_ERR_INVALID_ARG;
+    }
+    if (!device_range_ok(residual, tensor_bytes, "residual", who) ||
+        !device_range_ok(weight, (uint64_t)h * es, "weight", who) ||
+        !device_range_ok(out, tensor_bytes, "out", who) ||
+        !device_range_ok(residual_out, tensor_bytes, "residual_out", who))
+      return TW_ERR_INVALID_ARG;
+  }
   return TW_OK;
 }
 
@@ -158,6 +206,10 @@ tw_status launch_rows(const void* const* partials, int32_t n, const void* residu
 extern "C" {
 
 int32_t tw_abi_version(void) { return TW_ABI_VERSION; }
+
+void tw_set_pointer_checks(int32_t enabled) {
+  tw::g_pointer_checks.store(enabled != 0 ? 1 : 0, std::memory_order_relaxed);
+}
 
 tw_status tw_fused_reduce_rmsnorm(const void* const* partials, int32_t num_partials,
                                   const void* residual, const void* weight, void* out,

@@ -133,6 +133,20 @@ def test_grid_entry_validates_workgroups(lib):
     assert lib.tw_fused_reduce_rmsnorm_grid(*bad, 8, None) == INVALID
 
 
+def test_pointer_checks_reject_unknown_memory(lib):
+    # With checks on, pointers the HIP runtime does not know (here: fake
+    # addresses, with no GPU at all) are rejected before any launch.
+    tw.tw_set_pointer_checks(True)
+    try:
+        assert _call(lib) == INVALID
+        assert b"partials[0]" in lib.tw_last_error()
+        assert _call(lib, T=0) == 0            # nothing to launch, nothing checked
+    finally:
+        tw.tw_set_pointer_checks(False)
+    assert _call(lib, eps=-1.0) == INVALID     # plain validation still first
+    assert b"eps" in lib.tw_last_error()
+
+
 def test_shard_index_range(lib):
     for k in (-1, 2, 100):
         assert _call(lib, shard=k) == INVALID

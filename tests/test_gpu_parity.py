@@ -342,3 +342,45 @@ def test_prepared_launches_match_direct_calls():
     assert cache(4096) == oracle.split_plan(4096, tokens_per_cta=256, ctas_per_token_tile=32,
                                             num_cus=256, min_split_tokens=1024)
     assert cache(4096) is cache(4096)
+
+
+
+@pytest.mark.parametrize("N", list(range(1, 17)))
+def test_every_partial_count_at_the_headline_width(N):
+    d = make_inputs("llama70b", num_tokens=12, hidden=8192, seed=100 + N)
+    d["partials"] = np.concatenate([d["partials"]] * 2)[:N]
+    parts, res, w = upload(d)
+    say(f"N={N} T=12 h=8192 (full and 5-workgroup grid)")
+    out, rout = _run_full(parts, res, w, d["eps"])
+    y, x, _ = _oracle(d)
+    check(out, y, "bf16", "out")
+    check(rout, x, "bf16", "residual_out")
+    o2, r2 = tw.tw_fused_reduce_rmsnorm_grid(parts, res, w, d["eps"], 5)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(o2), out)
+    np.testing.assert_array_equal(to_host(r2), rout)
+
+
+def test_pointer_checks_reject_host_memory():
+    d = make_inputs("llama70b", num_tokens=16, hidden=1024)
+    parts, res, w = upload(d)
+    host_part = torch.empty((16, 1024), dtype=torch.bfloat16, pin_memory=True)
+    host_part.copy_(parts[0].cpu())
+    tw.tw_set_pointer_checks(True)
+    try:
+        say("pointer checks on: device tensors pass")
+        out, _ = tw.tw_fused_reduce_rmsnorm(parts, res, w, d["eps"])
+        torch.cuda.synchronize()
+        say("pointer checks on: a pinned host partial is rejected before launch")
+        lib = tw.load_library()
+        import ctypes
+        ptrs = (ctypes.c_void_p * 2)(host_part.data_ptr(), parts[1].data_ptr())
+        o = torch.empty_like(res)
+        r = torch.empty_like(res)
+        st = lib.tw_fused_reduce_rmsnorm(ptrs, 2, res.data_ptr(), w.data_ptr(), o.data_ptr(),
+                                         r.data_ptr(), 16, 1024, ctypes.c_float(1e-5), 1, None)
+        assert st == 1 and b"not device memory" in lib.tw_last_error()
+    finally:
+        tw.tw_set_pointer_checks(False)
+    ref, _ = _run_full(parts, res, w, d["eps"])
+    np.testing.assert_array_equal(to_host(out), ref)
