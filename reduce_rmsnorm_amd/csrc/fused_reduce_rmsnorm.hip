@@ -193,18 +193,18 @@ __global__ __launch_bounds__(BLOCK) void fused_reduce_rmsnorm_rows_kernel(KArgs 
 using KernelFn = void (*)(KArgs);
 using RowsKernelFn = void (*)(KArgs, int64_t, int64_t);
 
-template <int N, int G> constexpr int kWavesPerEu =
-    N <= kMaxCappedPartials ? kGeometry[G].waves_per_eu : 1;
-
 template <bool BF16, int G, int... Ns>
 constexpr std::array<KernelFn, sizeof...(Ns)> row_of(std::integer_sequence<int, Ns...>) {
-  return {&fused_reduce_rmsnorm_kernel<Ns + 1, kGeometry[G].block, kGeometry[G].vpt, BF16,
-                                       kWavesPerEu<Ns + 1, G>, kGeometry[G].chunk>...};
+  return {&fused_reduce_rmsnorm_kernel<Ns + 1, fused_geometry(G, Ns + 1).block,
+                                       fused_geometry(G, Ns + 1).vpt, BF16,
+                                       fused_geometry(G, Ns + 1).waves_per_eu,
+                                       fused_geometry(G, Ns + 1).chunk>...};
 }
 template <bool BF16, int G, int... Ns>
 constexpr std::array<RowsKernelFn, sizeof...(Ns)> rows_row_of(std::integer_sequence<int, Ns...>) {
-  return {&fused_reduce_rmsnorm_rows_kernel<Ns + 1, kGeometry[G].block, kGeometry[G].vpt, BF16,
-                                            kGeometry[G].chunk>...};
+  return {&fused_reduce_rmsnorm_rows_kernel<Ns + 1, fused_geometry(G, Ns + 1).block,
+                                            fused_geometry(G, Ns + 1).vpt, BF16,
+                                            fused_geometry(G, Ns + 1).chunk>...};
 }
 
 template <bool BF16, int... Gs>
@@ -225,11 +225,12 @@ const auto kRowsTableBF16 = rows_table_of<true>(std::make_integer_sequence<int, 
 
 }  // namespace
 
-void kernel_geometry(int64_t hidden, int32_t elem_bytes, int* block, int* vecs_per_thread) {
+void kernel_geometry(int64_t hidden, int32_t elem_bytes, int32_t num_partials, int* block,
+                     int* vecs_per_thread) {
   const int64_t nvec = hidden * elem_bytes / 16;
   const int g = geometry_index(nvec);
-  *block = g < 0 ? 0 : kGeometry[g].block;
-  *vecs_per_thread = g < 0 ? 0 : kGeometry[g].vpt;
+  *block = g < 0 ? 0 : fused_geometry(g, num_partials).block;
+  *vecs_per_thread = g < 0 ? 0 : fused_geometry(g, num_partials).vpt;
 }
 
 int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
@@ -253,12 +254,13 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
   k.hidden = (float)L.hidden;
   k.eps = L.eps;
 
+  const int block = fused_geometry(g, L.num_partials).block;
   hipError_t e;
   if (L.max_workgroups <= 0 || L.max_workgroups >= L.num_rows) {
     const KernelFn fn = bf16 ? kTableBF16[g][L.num_partials - 1] : kTableF32[g][L.num_partials - 1];
     void* args[] = {&k};
     e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)L.num_rows),
-                        dim3(kGeometry[g].block), args, 0, static_cast<hipStream_t>(L.stream));
+                        dim3(block), args, 0, static_cast<hipStream_t>(L.stream));
   } else {
     const RowsKernelFn fn =
         bf16 ? kRowsTableBF16[g][L.num_partials - 1] : kRowsTableF32[g][L.num_partials - 1];
@@ -266,8 +268,8 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
     int64_t row_end = L.row_begin + L.num_rows;
     const unsigned grid = (unsigned)((L.num_rows + rows_per_wg - 1) / rows_per_wg);
     void* args[] = {&k, &rows_per_wg, &row_end};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(kGeometry[g].block),
-                        args, 0, static_cast<hipStream_t>(L.stream));
+    e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(block), args, 0,
+                        static_cast<hipStream_t>(L.stream));
   }
   if (e != hipSuccess) {
     std::snprintf(err, errlen, "hipLaunchKernel: %s", hipGetErrorString(e));

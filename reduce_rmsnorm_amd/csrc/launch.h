@@ -56,9 +56,11 @@ struct AddNormLaunch {
 };
 int launch_add_rmsnorm(const AddNormLaunch& a, char* err, size_t errlen);
 
-// Threads per workgroup and 16-byte vectors per thread that the kernel uses
-// for a given hidden size and element size.  Depends on nothing else, so every
-// launch over rows of the same width runs the same per-row code.
-void kernel_geometry(int64_t hidden, int32_t elem_bytes, int* block, int* vecs_per_thread);
+// Threads per workgroup and 16-byte vectors per thread that the fused kernel
+// uses for a given hidden size, element size and partial count.  Depends on
+// nothing else, so every launch over rows of the same shape runs the same
+// per-row code.
+void kernel_geometry(int64_t hidden, int32_t elem_bytes, int32_t num_partials, int* block,
+                     int* vecs_per_thread);
 
 }  // namespace tw
