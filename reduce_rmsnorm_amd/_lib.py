@@ -221,8 +221,16 @@ def tw_reduce_partials(partials, reduced: Optional[torch.Tensor] = None,
     ref = parts[0]
     if ref.dim() != 2:
         raise ValueError("partials must be [T, h]")
-    weight_stub = ref[0] if ref.shape[0] > 0 else ref.new_empty((ref.shape[1],))
-    parts, ptrs, T, h, reduced, _ = _marshal(parts, ref, weight_stub, reduced, ref)
+    for p in parts:
+        if not p.is_cuda or p.dtype != ref.dtype or not p.is_contiguous() or p.shape != ref.shape:
+            raise ValueError("partials must be contiguous GPU tensors of one shape and dtype")
+    if reduced is None:
+        reduced = torch.empty_like(ref)
+    if reduced.shape != ref.shape or reduced.dtype != ref.dtype or not reduced.is_contiguous() \
+            or reduced.device != ref.device:
+        raise ValueError("reduced must be a contiguous tensor like the partials")
+    T, h = ref.shape
+    ptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
     with torch.cuda.device(ref.device):
         _check(lib.tw_reduce_partials(ptrs, len(parts), reduced.data_ptr(), T, h,
                                       _dtype_code(ref), _stream_handle(ref.device, stream)))

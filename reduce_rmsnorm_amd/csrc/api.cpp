@@ -60,22 +60,29 @@ bool device_range_ok(const void* p, uint64_t bytes, const char* what, const char
   return true;
 }
 
-struct Range {
-  uintptr_t lo, hi;   // [lo, hi)
+// One tensor argument of an entry point: where it is, how many bytes the call
+// touches, its name in messages, and whether the call writes it.
+struct Tensor {
+  const void* p;
+  uint64_t bytes;
+  char name[24];
+  bool output;
 };
 
-bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
-
-Range range_of(const void* p, uint64_t bytes) {
-  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-  return Range{lo, lo + (uintptr_t)bytes};
+Tensor tensor(const void* p, uint64_t bytes, const char* name, bool output) {
+  Tensor t{p, bytes, {}, output};
+  std::snprintf(t.name, sizeof(t.name), "%s", name);
+  return t;
 }
 
-// Shared checks of the fused and shard entries; TW_OK when the arguments are
-// valid.  With num_tokens == 0 the pointers are not inspected.
-tw_status validate(const void* const* partials, int32_t n, const void* residual,
-                   const void* weight, void* out, void* residual_out, int64_t T, int64_t h,
-                   float eps, tw_dtype dtype, const char* who, bool outputs_alias = false) {
+bool overlap(const Tensor& a, const Tensor& b) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Scalar arguments shared by every row entry point.  Sets *elem_bytes.
+tw_status check_scalars(int32_t n, int64_t T, int64_t h, float eps, tw_dtype dtype,
+                        const char* who, int64_t* elem_bytes) {
   if (n < 1 || n > TW_MAX_PARTIALS) {
     set_error("%s: num_partials=%d outside [1, %d]", who, n, TW_MAX_PARTIALS);
     return TW_ERR_INVALID_ARG;
@@ -108,69 +115,76 @@ tw_status validate(const void* const* partials, int32_t n, const void* residual,
     set_error("%s: num_tokens=%lld exceeds %lld", who, (long long)T, (long long)TW_MAX_TOKENS);
     return TW_ERR_UNSUPPORTED;
   }
-  if (T == 0) return TW_OK;
-  if (partials == nullptr || residual == nullptr || weight == nullptr || out == nullptr ||
-      residual_out == nullptr) {
-    set_error("%s: NULL tensor pointer", who);
-    return TW_ERR_INVALID_ARG;
-  }
-  for (int32_t i = 0; i < n; ++i) {
-    if (partials[i] == nullptr) {
-      set_error("%s: partials[%d] is NULL", who, i);
+  *elem_bytes = es;
+  return TW_OK;
+}
+
+// Tensor arguments: none NULL, all 16-byte aligned, no output overlapping any
+// other argument except the one allowed in-place pair (output t[in_place_out]
+// at exactly the address of input t[in_place_in]; -1: none), and, with pointer
+// checks on, all device memory inside one allocation each.
+tw_status check_tensors(const Tensor* t, int count, const char* who, int in_place_out = -1,
+                        int in_place_in = -1) {
+  for (int i = 0; i < count; ++i) {
+    if (t[i].p == nullptr) {
+      set_error("%s: %s is NULL", who, t[i].name);
       return TW_ERR_INVALID_ARG;
     }
   }
-  auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
-  for (int32_t i = 0; i < n; ++i) {
-    if (misaligned(partials[i])) {
-      set_error("%s: partials[%d] is not 16-byte aligned", who, i);
+  for (int i = 0; i < count; ++i) {
+    if ((reinterpret_cast<uintptr_t>(t[i].p) & 15u) != 0) {
+      set_error("%s: %s is not 16-byte aligned", who, t[i].name);
       return TW_ERR_UNSUPPORTED;
     }
   }
-  if (misaligned(residual) || misaligned(weight) || misaligned(out) || misaligned(residual_out)) {
-    set_error("%s: residual, weight, out and residual_out must be 16-byte aligned", who);
-    return TW_ERR_UNSUPPORTED;
-  }
-  const uint64_t tensor_bytes = (uint64_t)T * (uint64_t)h * (uint64_t)es;
-  const Range r_out = range_of(out, tensor_bytes);
-  const Range r_res_out = range_of(residual_out, tensor_bytes);
-  const Range r_res = range_of(residual, tensor_bytes);
-  const Range r_w = range_of(weight, (uint64_t)h * es);
-  if (!outputs_alias && overlaps(r_out, r_res_out)) {
-    set_error("%s: out and residual_out overlap", who);
-    return TW_ERR_INVALID_ARG;
-  }
-  // With outputs_alias the caller has one output (passed as both) and the
-  // residual/weight slots hold a partial; only the partials are checked.
-  const bool in_place = residual_out == residual;
-  const int32_t last_input = outputs_alias ? n - 1 : n + 1;
-  for (int32_t i = 0; i <= last_input; ++i) {
-    const Range in = i < n ? range_of(partials[i], tensor_bytes) : (i == n ? r_res : r_w);
-    if (overlaps(r_out, in)) {
-      set_error("%s: out overlaps an input (%s)", who,
-                i < n ? "a partial" : (i == n ? "residual" : "weight"));
-      return TW_ERR_INVALID_ARG;
-    }
-    if (i == n && in_place) continue;
-    if (overlaps(r_res_out, in)) {
-      set_error("%s: residual_out overlaps an input (%s); only residual_out == residual is "
-                "allowed", who, i < n ? "a partial" : (i == n ? "residual" : "weight"));
-      return TW_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i) {
+    if (!t[i].output) continue;
+    for (int j = 0; j < count; ++j) {
+      if (j == i || (t[j].output && j < i)) continue;     // each output pair once
+      // The exemption is for that one pair, at exactly the same address.
+      const bool allowed = i == in_place_out && j == in_place_in && t[i].p == t[j].p &&
+                           t[i].bytes == t[j].bytes;
+      if (!allowed && overlap(t[i], t[j])) {
+        set_error("%s: %s overlaps %s%s", who, t[i].name, t[j].name,
+                  in_place_out >= 0 ? " (only residual_out == residual is allowed)" : "");
+        return TW_ERR_INVALID_ARG;
+      }
     }
   }
   if (g_pointer_checks.load(std::memory_order_relaxed)) {
-    char what[32];
-    for (int32_t i = 0; i < n; ++i) {
-      std::snprintf(what, sizeof(what), "partials[%d]", i);
-      if (!device_range_ok(partials[i], tensor_bytes, what, who)) return TW_ERR_INVALID_ARG;
-    }
-    if (!device_range_ok(residual, tensor_bytes, "residual", who) ||
-        !device_range_ok(weight, (uint64_t)h * es, "weight", who) ||
-        !device_range_ok(out, tensor_bytes, "out", who) ||
-        !device_range_ok(residual_out, tensor_bytes, "residual_out", who))
-      return TW_ERR_INVALID_ARG;
+    for (int i = 0; i < count; ++i)
+      if (!device_range_ok(t[i].p, t[i].bytes, t[i].name, who)) return TW_ERR_INVALID_ARG;
   }
   return TW_OK;
+}
+
+// Validation of the fused, shard and grid entries (and of tw_add_rmsnorm with
+// its input as the one partial).  With num_tokens == 0 the pointers are not
+// inspected.
+tw_status validate(const void* const* partials, int32_t n, const void* residual,
+                   const void* weight, void* out, void* residual_out, int64_t T, int64_t h,
+                   float eps, tw_dtype dtype, const char* who,
+                   const char* partial_name = "partials") {
+  int64_t es = 0;
+  const tw_status s = check_scalars(n, T, h, eps, dtype, who, &es);
+  if (s != TW_OK || T == 0) return s;
+  if (partials == nullptr) {
+    set_error("%s: %s array is NULL", who, partial_name);
+    return TW_ERR_INVALID_ARG;
+  }
+  const uint64_t tb = (uint64_t)T * (uint64_t)h * (uint64_t)es;
+  Tensor t[TW_MAX_PARTIALS + 4];
+  char name[24];
+  for (int32_t i = 0; i < n; ++i) {
+    if (n == 1 && partial_name[0] != 'p') std::snprintf(name, sizeof(name), "%s", partial_name);
+    else std::snprintf(name, sizeof(name), "%s[%d]", partial_name, i);
+    t[i] = tensor(partials[i], tb, name, false);
+  }
+  t[n] = tensor(residual, tb, "residual", false);
+  t[n + 1] = tensor(weight, (uint64_t)h * es, "weight", false);
+  t[n + 2] = tensor(out, tb, "out", true);
+  t[n + 3] = tensor(residual_out, tb, "residual_out", true);
+  return check_tensors(t, n + 4, who, /*in_place_out=*/n + 3, /*in_place_in=*/n);
 }
 
 tw_status launch_rows(const void* const* partials, int32_t n, const void* residual,
@@ -260,18 +274,24 @@ tw_status tw_shard_rmsnorm(const void* const* partials, int32_t num_partials,
 
 tw_status tw_reduce_partials(const void* const* partials, int32_t num_partials, void* reduced,
                              int64_t num_tokens, int64_t hidden, tw_dtype dtype, void* stream) {
-  // Same checks as the fused entry with the reduced tensor standing in for
-  // both outputs' ranges; a zero eps and the partials as residual/weight
-  // placeholders keep the shared validation meaningful.
   const char* who = "tw_reduce_partials";
-  if (num_tokens > 0 && reduced == nullptr) {
-    tw::set_error("%s: NULL tensor pointer", who);
+  int64_t es = 0;
+  tw_status s = tw::check_scalars(num_partials, num_tokens, hidden, 0.0f, dtype, who, &es);
+  if (s != TW_OK || num_tokens == 0) return s;
+  if (partials == nullptr) {
+    tw::set_error("%s: partials array is NULL", who);
     return TW_ERR_INVALID_ARG;
   }
-  const void* any = (partials != nullptr && num_partials >= 1) ? partials[0] : nullptr;
-  tw_status s = tw::validate(partials, num_partials, any, any, reduced, reduced, num_tokens,
-                             hidden, 0.0f, dtype, who, /*outputs_alias=*/true);
-  if (s != TW_OK || num_tokens == 0) return s;
+  const uint64_t tb = (uint64_t)num_tokens * (uint64_t)hidden * (uint64_t)es;
+  tw::Tensor t[TW_MAX_PARTIALS + 1];
+  char name[24];
+  for (int32_t i = 0; i < num_partials; ++i) {
+    std::snprintf(name, sizeof(name), "partials[%d]", i);
+    t[i] = tw::tensor(partials[i], tb, name, false);
+  }
+  t[num_partials] = tw::tensor(reduced, tb, "reduced", true);
+  s = tw::check_tensors(t, num_partials + 1, who);
+  if (s != TW_OK) return s;
   tw::ReduceLaunch L{};
   for (int32_t i = 0; i < num_partials; ++i) L.partials[i] = partials[i];
   L.num_partials = num_partials;
@@ -293,7 +313,7 @@ tw_status tw_add_rmsnorm(const void* input, const void* residual, const void* we
                          tw_dtype dtype, void* stream) {
   const void* parts[1] = {input};
   const tw_status s = tw::validate(parts, 1, residual, weight, out, residual_out, num_tokens,
-                                   hidden, eps, dtype, "tw_add_rmsnorm");
+                                   hidden, eps, dtype, "tw_add_rmsnorm", "input");
   if (s != TW_OK || num_tokens == 0) return s;
   tw::AddNormLaunch L{};
   L.input = input;

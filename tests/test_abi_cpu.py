@@ -81,24 +81,24 @@ def _call(lib, n=2, T=4, h=64, eps=1e-5, dtype=1, parts=None, res=A + 10 * MB, w
     (dict(h=65544), UNSUPPORTED, "exceeds"),
     (dict(h=32772, dtype=0), UNSUPPORTED, "exceeds"),
     (dict(T=2 ** 31), UNSUPPORTED, "exceeds"),
-    (dict(parts=False), INVALID, "NULL"),
+    (dict(parts=False), INVALID, "partials array is NULL"),
     (dict(parts=[A, 0]), INVALID, "partials[1] is NULL"),
-    (dict(res=0), INVALID, "NULL"),
-    (dict(w=0), INVALID, "NULL"),
-    (dict(out=0), INVALID, "NULL"),
-    (dict(rout=0), INVALID, "NULL"),
-    (dict(parts=[A, A + MB + 8]), UNSUPPORTED, "aligned"),
-    (dict(res=A + 10 * MB + 4), UNSUPPORTED, "aligned"),
-    (dict(w=A + 11 * MB + 2), UNSUPPORTED, "aligned"),
-    (dict(out=A + 12 * MB + 8), UNSUPPORTED, "aligned"),
-    (dict(rout=A + 13 * MB + 8), UNSUPPORTED, "aligned"),
-    (dict(out=A + 13 * MB + 16), INVALID, "out and residual_out overlap"),
-    (dict(out=A), INVALID, "out overlaps an input (a partial)"),
-    (dict(out=A + 10 * MB + 256), INVALID, "out overlaps an input (residual)"),
-    (dict(out=A + 11 * MB), INVALID, "out overlaps an input (weight)"),
-    (dict(rout=A + MB), INVALID, "residual_out overlaps an input (a partial)"),
-    (dict(rout=A + 10 * MB + 16), INVALID, "residual_out overlaps an input (residual)"),
-    (dict(rout=A + 11 * MB - 16), INVALID, "residual_out overlaps an input (weight)"),
+    (dict(res=0), INVALID, "residual is NULL"),
+    (dict(w=0), INVALID, "weight is NULL"),
+    (dict(out=0), INVALID, "out is NULL"),
+    (dict(rout=0), INVALID, "residual_out is NULL"),
+    (dict(parts=[A, A + MB + 8]), UNSUPPORTED, "partials[1] is not 16-byte aligned"),
+    (dict(res=A + 10 * MB + 4), UNSUPPORTED, "residual is not 16-byte aligned"),
+    (dict(w=A + 11 * MB + 2), UNSUPPORTED, "weight is not 16-byte aligned"),
+    (dict(out=A + 12 * MB + 8), UNSUPPORTED, "out is not 16-byte aligned"),
+    (dict(rout=A + 13 * MB + 8), UNSUPPORTED, "residual_out is not 16-byte aligned"),
+    (dict(out=A + 13 * MB + 16), INVALID, "out overlaps residual_out"),
+    (dict(out=A), INVALID, "out overlaps partials[0]"),
+    (dict(out=A + 10 * MB + 256), INVALID, "out overlaps residual"),
+    (dict(out=A + 11 * MB), INVALID, "out overlaps weight"),
+    (dict(rout=A + MB), INVALID, "residual_out overlaps partials[1]"),
+    (dict(rout=A + 10 * MB + 16), INVALID, "residual_out overlaps residual"),
+    (dict(rout=A + 11 * MB - 16), INVALID, "residual_out overlaps weight"),
 ])
 def test_invalid_arguments_rejected_before_any_device_call(lib, kw, code, needle, shard):
     assert _call(lib, shard=shard, **kw) == code
@@ -110,7 +110,7 @@ def test_unfused_entries_validate(lib):
     assert lib.tw_reduce_partials(arr, 0, A + 12 * MB, 4, 64, 1, None) == INVALID
     assert lib.tw_reduce_partials(arr, 2, None, 4, 64, 1, None) == INVALID
     assert lib.tw_reduce_partials(arr, 2, A + 16, 4, 64, 1, None) == INVALID     # overlaps partial 0
-    assert b"overlaps" in lib.tw_last_error()
+    assert b"reduced overlaps partials[0]" in lib.tw_last_error()
     assert lib.tw_reduce_partials(arr, 2, A + 12 * MB + 8, 4, 64, 1, None) == UNSUPPORTED
     assert lib.tw_reduce_partials(arr, 2, A + 12 * MB, 4, 12, 1, None) == UNSUPPORTED
     assert lib.tw_reduce_partials(None, 2, None, 0, 64, 1, None) == 0           # T == 0: no-op
@@ -118,6 +118,11 @@ def test_unfused_entries_validate(lib):
     assert lib.tw_add_rmsnorm(*args, ctypes.c_float(-1.0), 1, None) == INVALID
     assert lib.tw_add_rmsnorm(A, A + 10 * MB, A + 11 * MB, A, A + 13 * MB, 4, 64,
                               ctypes.c_float(1e-5), 1, None) == INVALID          # out == input
+    assert b"out overlaps input" in lib.tw_last_error()
+    # residual_out may replace the residual in place
+    assert lib.tw_add_rmsnorm(A, A + 10 * MB, A + 11 * MB, A + 12 * MB, A + 10 * MB, 4, 64,
+                              ctypes.c_float(-1.0), 1, None) == INVALID
+    assert b"eps" in lib.tw_last_error()
     assert lib.tw_add_rmsnorm(0, 0, 0, 0, 0, 0, 64, ctypes.c_float(1e-5), 1, None) == 0
 
 
@@ -170,9 +175,19 @@ def test_adjacent_buffers_do_not_overlap(lib):
 
 
 def test_in_place_residual_is_allowed_by_validation(lib):
-    # residual_out == residual passes the overlap check; eps makes it fail later.
-    assert _call(lib, rout=A + 10 * MB, eps=-1.0) == INVALID
-    assert b"eps" in lib.tw_last_error()
+    # residual_out == residual passes the overlap check (with pointer checks
+    # on, the fake addresses are then rejected as unknown memory, not as an
+    # overlap); out == residual and a shifted residual_out are not allowed.
+    tw.tw_set_pointer_checks(True)
+    try:
+        assert _call(lib, rout=A + 10 * MB) == INVALID
+        assert b"overlap" not in lib.tw_last_error()
+    finally:
+        tw.tw_set_pointer_checks(False)
+    assert _call(lib, out=A + 10 * MB) == INVALID
+    assert b"out overlaps residual" in lib.tw_last_error()
+    assert _call(lib, rout=A + 10 * MB + 16) == INVALID
+    assert b"residual_out overlaps residual" in lib.tw_last_error()
 
 
 # --------------------------------------------------------------- planner ----
@@ -243,3 +258,38 @@ def test_planner_null_and_limits(lib):
     with pytest.raises(tw.TokenWeaveError) as e:    # 2^40 waves do not fit int32
         tw.tw_split_plan(2 ** 40, num_cus=1)
     assert e.value.status == UNSUPPORTED
+
+
+def test_overlap_validation_matches_brute_force(lib):
+    # Random placements of 2 partials, residual, weight, out and residual_out
+    # on a small grid of 16-byte-aligned addresses.  With pointer checks on, a
+    # layout that passes the overlap rule stops at "memory the runtime does
+    # not know" (fake addresses), so nothing ever launches; a layout that
+    # breaks it must be reported as an overlap.  The rule: an output may not
+    # share a byte with any other tensor, except residual_out == residual.
+    rng = random.Random(5)
+    T, h = 2, 64
+    tb, wb = T * h * 2, h * 2
+    tw.tw_set_pointer_checks(True)
+    try:
+        for _ in range(600):
+            addr = {k: A + 16 * rng.randrange(0, 96) for k in ("p0", "p1", "res", "w", "out", "rout")}
+            if rng.random() < 0.2:
+                addr["rout"] = addr["res"]
+            size = {"p0": tb, "p1": tb, "res": tb, "w": wb, "out": tb, "rout": tb}
+
+            def ov(a, b):
+                return addr[a] < addr[b] + size[b] and addr[b] < addr[a] + size[a]
+            bad = False
+            for o in ("out", "rout"):
+                for k in size:
+                    if k == o or (o == "rout" and k == "res" and addr["rout"] == addr["res"]):
+                        continue
+                    bad |= ov(o, k)
+            st = _call(lib, T=T, h=h, parts=[addr["p0"], addr["p1"]], res=addr["res"], w=addr["w"],
+                       out=addr["out"], rout=addr["rout"])
+            msg = lib.tw_last_error().decode()
+            assert st == INVALID, (addr, st, msg)
+            assert ("overlaps" in msg) == bad, (addr, msg)
+    finally:
+        tw.tw_set_pointer_checks(False)
