@@ -69,6 +69,9 @@ def parse():
                     help="also time one tensor-parallel layer step (row-parallel GEMM + fused "
                          "step) unsplit and split in two on two streams, for every offset, at "
                          "several token counts: the measured offset sweep")
+    ap.add_argument("--split-table", action="store_true",
+                    help="also time the fused step alone as two launches (prefix, suffix) for "
+                         "every offset, next to one launch over all rows")
     ap.add_argument("--ceiling", action="store_true",
                     help="also time the bandwidth probes on the same buffers: N+1 streamed reads "
                          "+ 2 streamed writes, reads only, writes only (the achievable envelope; "
@@ -383,6 +386,38 @@ def main():
             print(f"[bench] footprint {G:5d} workgroups: {g_us:9.2f} us  {gbs_g:7.1f} GB/s",
                   file=sys.stderr, flush=True)
 
+    split_table = None
+    if args.split_table and args.mode == "full":
+        split_table = []
+        half = T // 2
+        for off in (None, 0, 64, 128, 192, 256, 512):
+            if off is not None and off >= half:
+                continue
+            P = T if off is None else half + off
+            piece_sets = []
+            for parts, res, out, rout in sets:
+                pieces = [(0, T)] if off is None else [(0, P), (P, T)]
+                piece_sets.append([tw.PreparedFused([p[lo:hi] for p in parts], res[lo:hi], w,
+                                                    wl.eps, out[lo:hi], rout[lo:hi], stream)
+                                   for lo, hi in pieces])
+            for i in range(20):
+                for launch in piece_sets[i % R]:
+                    launch()
+            torch.cuda.synchronize()
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for i in range(args.steps):
+                for launch in piece_sets[i % R]:
+                    launch()
+            s1.record(stream)
+            torch.cuda.synchronize()
+            us = s0.elapsed_time(s1) * 1e3 / args.steps
+            split_table.append({"offset": off, "prefix": P, "suffix": T - P, "us": round(us, 2),
+                                "gbs": round(step_bytes / (us * 1e-6) / 1e9, 1)})
+            print(f"[bench] split table offset {off}: prefix {P} suffix {T - P}: {us:.2f} us "
+                  f"({split_table[-1]['gbs']} GB/s)", file=sys.stderr, flush=True)
+
     overlap = None
     if args.overlap:
         overlap = run_overlap(tw, torch, wl, plan_kw)
@@ -442,6 +477,8 @@ def main():
         result["footprint"] = footprint
     if overlap is not None:
         result["overlap"] = overlap
+    if split_table is not None:
+        result["split_table"] = split_table
     if ceiling is not None:
         result["ceiling"] = ceiling
     if args.cpu_seconds > 0:

@@ -293,3 +293,25 @@ def test_overlap_validation_matches_brute_force(lib):
             assert ("overlaps" in msg) == bad, (addr, msg)
     finally:
         tw.tw_set_pointer_checks(False)
+
+
+def test_last_error_is_per_thread(lib):
+    # Each host thread sees the message of its own last failing call.
+    import threading
+    results = {}
+
+    def worker(k):
+        for _ in range(200):
+            if k == 0:
+                _call(lib, eps=-1.0)
+            else:
+                _call(lib, h=12)
+            results.setdefault(k, set()).add(lib.tw_last_error())
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in (0, 1)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert all(b"eps" in m for m in results[0])
+    assert all(b"multiple" in m for m in results[1])

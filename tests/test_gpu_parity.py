@@ -384,3 +384,23 @@ def test_pointer_checks_reject_host_memory():
         tw.tw_set_pointer_checks(False)
     ref, _ = _run_full(parts, res, w, d["eps"])
     np.testing.assert_array_equal(to_host(out), ref)
+
+
+def test_nan_input_propagates_to_its_row_only():
+    # NaN and inf are outside the contract; the documented behaviour is that
+    # they propagate: a NaN in one row makes that row's outputs NaN (its sum
+    # of squares is NaN) and leaves every other row exact.
+    d = make_inputs("llama70b", num_tokens=6, hidden=4096)
+    d["partials"] = d["partials"].copy()
+    d["partials"][2, 3, 100] = 0x7FC0          # quiet NaN in row 3
+    parts, res, w = upload(d)
+    say("NaN in one partial element")
+    out, rout = _run_full(parts, res, w, d["eps"])
+    val = oracle.bf16_bits_to_f64(out)
+    assert np.isnan(val[3]).all()
+    rval = oracle.bf16_bits_to_f64(rout)
+    assert np.isnan(rval[3, 100]) and np.isfinite(np.delete(rval[3], 100)).all()
+    keep = [0, 1, 2, 4, 5]
+    y, x, _ = _oracle(d, rows=keep)
+    check(out[keep], y, "bf16", "out")
+    check(rout[keep], x, "bf16", "residual_out")
