@@ -72,6 +72,10 @@ def parse():
     ap.add_argument("--split-table", action="store_true",
                     help="also time the fused step alone as two launches (prefix, suffix) for "
                          "every offset, next to one launch over all rows")
+    ap.add_argument("--cu-mask", action="store_true",
+                    help="also run the fused kernel on CU-masked streams: where mask bits land "
+                         "(XCD, CU), GB/s against the number of CUs, and the split layer step "
+                         "with the fused kernel and the GEMM on disjoint CU sets")
     ap.add_argument("--ceiling", action="store_true",
                     help="also time the bandwidth probes on the same buffers: N+1 streamed reads "
                          "+ 2 streamed writes, reads only, writes only (the achievable envelope; "
@@ -84,12 +88,7 @@ def run_ceiling(sets, R, rows, h, itemsize, stream, steps, timer):
     own rotated buffers: sources are the partial rows and the residual rows,
     destinations are out and residual_out."""
     import ctypes
-    from reduce_rmsnorm_amd.build import PROBE_LIB_PATH
-    lib = ctypes.CDLL(PROBE_LIB_PATH)
-    lib.tw_probe_launch.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
-                                    ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int64,
-                                    ctypes.c_int, ctypes.c_void_p]
-    lib.tw_probe_launch.restype = ctypes.c_int
+    lib = _probe_lib()
     tensor_bytes = rows * h * itemsize
     nvec = tensor_bytes // 16
     ptrs = []
@@ -195,6 +194,134 @@ def run_overlap(tw, torch, wl, plan_kw) -> list:
         del step
         torch.cuda.empty_cache()
     return rows
+
+
+def _probe_lib():
+    import ctypes
+    from reduce_rmsnorm_amd.build import PROBE_LIB_PATH
+    lib = ctypes.CDLL(PROBE_LIB_PATH)
+    lib.tw_probe_launch.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int64,
+                                    ctypes.c_int, ctypes.c_void_p]
+    lib.tw_probe_launch.restype = ctypes.c_int
+    return lib
+
+
+PLACEMENT_GRID = 4096
+
+
+def placement(lib, torch, stream, records):
+    """Run the placement probe on ``stream``: returns {XCC id: number of
+    distinct CUs its workgroups ran on}.  A CU is identified by its XCC id and
+    bits [15:8] of HW_ID (CU, shader array and shader engine ids)."""
+    import ctypes
+    import numpy as np
+    records.zero_()
+    dst = (ctypes.c_void_p * 1)(records.data_ptr())
+    src = (ctypes.c_void_p * 1)()
+    torch.cuda.current_stream().synchronize()
+    rc = lib.tw_probe_launch(3, src, 0, dst, 1, PLACEMENT_GRID, PLACEMENT_GRID, stream.cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"placement probe launch failed: {rc}")
+    stream.synchronize()
+    r = records.cpu().numpy().view(np.uint32).reshape(PLACEMENT_GRID, 4)
+    if not (r[:, 3] == 1).all():
+        raise RuntimeError("placement probe left records unwritten")
+    cus = {}
+    for xcc, loc in set(zip((r[:, 1] & 0xF).tolist(), ((r[:, 0] >> 8) & 0xFF).tolist())):
+        cus[xcc] = cus.get(xcc, 0) + 1
+    return dict(sorted(cus.items()))
+
+
+def run_cu_mask(tw, torch, wl, sets, R, w, step_bytes) -> dict:
+    """CU-masked streams (``hipExtStreamCreateWithCUMask``).
+
+    The runtime accepts a mask only if it leaves at least one CU on each of the
+    eight XCDs (a dispatch's workgroups are dealt out over all of them), and
+    mask bit b belongs to XCD b mod 8; the placement probe confirms both here by
+    counting the CUs each XCD used.  Then: (1) fused-kernel GB/s on the first k
+    mask bits, which spreads k CUs evenly over the XCDs; (2) a skewed mask, one
+    XCD whole and one CU on each other XCD, against a balanced mask of about
+    the same size; (3) the split layer step with the fused kernel confined to k
+    CUs while the GEMM keeps an unmasked stream.
+
+    Only the fused kernel and the placement probe run on masked streams: their
+    workgroups never wait on one another, so confining them cannot stall a
+    launch.  The library GEMM's kernels are not known to have that property, so
+    they are never confined."""
+    from reduce_rmsnorm_amd.overlap import LayerStep, MaskedStream, time_steps
+    lib = _probe_lib()
+    records = torch.zeros(PLACEMENT_GRID * 4, dtype=torch.int32, device="cuda")
+    out = {}
+
+    checks = {"all 256 bits": list(range(256)), "bits 0-7": list(range(8)),
+              "bits 0-15": list(range(16)), "bits 0-7 + 8, 16, 24": list(range(8)) + [8, 16, 24]}
+    out["placement"] = {}
+    for name, bits in checks.items():
+        with MaskedStream(bits) as ms:
+            per_xcc = placement(lib, torch, ms.stream, records)
+        out["placement"][name] = per_xcc
+        print(f"[bench] cu-mask placement {name}: CUs used per XCD {per_xcc}",
+              file=sys.stderr, flush=True)
+
+    def time_fused(bits):
+        with MaskedStream(bits) as ms:
+            per_xcc = placement(lib, torch, ms.stream, records)
+            launches = [tw.PreparedFused(parts, res, w, wl.eps, o, ro, ms.stream)
+                        for parts, res, o, ro in sets]
+            for i in range(3):
+                launches[i % R]()
+            ms.stream.synchronize()
+            est_us = step_bytes / (36e9 * len(bits)) * 1e6
+            iters = max(5, min(2000, int(40e3 / est_us)))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(ms.stream)
+            for i in range(iters):
+                launches[i % R]()
+            e1.record(ms.stream)
+            ms.stream.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / iters
+        return us, per_xcc
+
+    foot = []
+    layouts = [(f"balanced {k}", list(range(k))) for k in (8, 16, 32, 40, 64, 128, 192, 256)]
+    layouts.insert(4, ("skewed 39: XCD 0 whole + 1 CU on each other XCD",
+                       list(range(0, 256, 8)) + list(range(1, 8))))
+    for name, bits in layouts:
+        us, per_xcc = time_fused(bits)
+        gbs = step_bytes / (us * 1e-6) / 1e9
+        foot.append({"layout": name, "cus": len(bits), "cus_per_xcd": list(per_xcc.values()),
+                     "us": round(us, 2), "gbs": round(gbs, 1)})
+        print(f"[bench] cu-mask footprint {name:50s} {us:9.2f} us {gbs:7.1f} GB/s "
+              f"(CUs per XCD {list(per_xcc.values())})", file=sys.stderr, flush=True)
+    out["footprint"] = foot
+
+    rows = []
+    default_a, default_b = torch.cuda.Stream(), torch.cuda.Stream()
+    for T in (4096, 8192):
+        step = LayerStep(T, wl.hidden, OVERLAP_K, wl.num_partials, eps=wl.eps, sets=2)
+        P = T // 2
+        iters = 40
+        base = time_steps(lambda i: step.run_unsplit(i, default_a), default_a, default_b, iters)
+        shared = time_steps(lambda i: step.run_split(i, P, default_a, default_b), default_a,
+                            default_b, iters)
+        entry = {"tokens": T, "prefix": P, "unsplit_us": round(base, 2),
+                 "split_shared_us": round(shared, 2), "split_fused_on_k_cus": []}
+        for k in (32, 64, 128, 192):
+            with MaskedStream(range(k)) as fa:
+                us = time_steps(lambda i: step.run_split(i, P, default_a, fa.stream),
+                                default_a, fa.stream, iters)
+            entry["split_fused_on_k_cus"].append({"cus": k, "us": round(us, 2)})
+        rows.append(entry)
+        print(f"[bench] cu-mask overlap T={T} (eager): unsplit {base:.1f} us, split on shared "
+              f"CUs {shared:.1f} us, split with the fused kernel on k CUs: " +
+              ", ".join(f"k={e['cus']}: {e['us']:.1f}" for e in entry["split_fused_on_k_cus"]),
+              file=sys.stderr, flush=True)
+        del step
+        torch.cuda.empty_cache()
+    out["overlap"] = rows
+    return out
 
 
 def cpu_baseline(wl, d, budget_s: float) -> dict:
@@ -386,6 +513,10 @@ def main():
             print(f"[bench] footprint {G:5d} workgroups: {g_us:9.2f} us  {gbs_g:7.1f} GB/s",
                   file=sys.stderr, flush=True)
 
+    cu_mask = None
+    if args.cu_mask and args.mode == "full":
+        cu_mask = run_cu_mask(tw, torch, wl, sets, R, w, step_bytes)
+
     split_table = None
     if args.split_table and args.mode == "full":
         split_table = []
@@ -479,6 +610,8 @@ def main():
         result["overlap"] = overlap
     if split_table is not None:
         result["split_table"] = split_table
+    if cu_mask is not None:
+        result["cu_mask"] = cu_mask
     if ceiling is not None:
         result["ceiling"] = ceiling
     if args.cpu_seconds > 0:

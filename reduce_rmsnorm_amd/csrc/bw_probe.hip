@@ -9,6 +9,10 @@
 //
 // Every probe walks 16-byte vectors [0, nvec) of each tensor with a grid-stride
 // loop; loads and stores are non-temporal, like the fused kernel's streams.
+//
+// A third kind of probe records where each workgroup ran (XCC and compute unit
+// as the hardware reports them), which shows how a stream's CU mask maps onto
+// the eight XCDs.
 
 #include <hip/hip_runtime.h>
 
@@ -78,6 +82,27 @@ __global__ __launch_bounds__(kBlock) void probe_write(ProbeArgs a) {
   }
 }
 
+// Hardware register reads (s_getreg immediates: size-1 in [15:11], bit offset in
+// [10:6], register id in [5:0]).  HW_ID (id 4) packs wave, SIMD, pipe, CU,
+// shader-array and shader-engine ids; XCC_ID (id 20) holds the XCD's index in
+// its low four bits.
+constexpr int kHwIdAll = (31 << 11) | 4;
+constexpr int kXccId = (3 << 11) | 20;
+constexpr int kPlacementBlock = 64;
+
+// One wave per workgroup.  Each workgroup stays resident for a short, fixed
+// time (so that the dispatcher spreads the grid over every CU it may use), then
+// lane 0 stores {HW_ID, XCC_ID, workgroup index, 1} at dst[0][workgroup].
+__global__ __launch_bounds__(kPlacementBlock) void probe_placement(ProbeArgs a) {
+  const unsigned hw = __builtin_amdgcn_s_getreg(kHwIdAll);
+  const unsigned xcc = __builtin_amdgcn_s_getreg(kXccId);
+  for (int k = 0; k < 32; ++k) __builtin_amdgcn_s_sleep(8);
+  if (threadIdx.x == 0 && (int64_t)blockIdx.x < a.nvec) {
+    const u32x4 rec = {hw, xcc, (unsigned)blockIdx.x, 1u};
+    a.dst[0][blockIdx.x] = rec;
+  }
+}
+
 using ProbeFn = void (*)(ProbeArgs);
 
 template <int... Ks>
@@ -93,13 +118,25 @@ const auto kRead = r_table(std::make_integer_sequence<int, kMaxStreams>{});
 
 }  // namespace
 
-// kind 0: read+write, 1: read only, 2: write only.  Returns 0 or a HIP error
-// code; -1 for arguments out of range.  nvec counts 16-byte vectors per tensor.
+// kind 0: read+write, 1: read only, 2: write only, 3: placement (one 16-byte
+// record per workgroup into dst[0], which must hold at least grid vectors).
+// Returns 0 or a HIP error code; -1 for arguments out of range.  nvec counts
+// 16-byte vectors per tensor.
 extern "C" int tw_probe_launch(int kind, const void* const* src, int nsrc, void* const* dst,
                                int ndst, int64_t nvec, int grid, void* stream) {
-  if (kind < 0 || kind > 2 || nsrc < 0 || nsrc > kMaxStreams || ndst < 0 || ndst > kMaxStreams ||
+  if (kind < 0 || kind > 3 || nsrc < 0 || nsrc > kMaxStreams || ndst < 0 || ndst > kMaxStreams ||
       nvec < 1 || grid < 1 || grid > 65536)
     return -1;
+  if (kind == 3) {
+    if (ndst != 1 || dst[0] == nullptr || nvec < grid) return -1;
+    ProbeArgs p{};
+    p.dst[0] = static_cast<u32x4*>(dst[0]);
+    p.ndst = 1;
+    p.nvec = nvec;
+    void* pargs[] = {&p};
+    return (int)hipLaunchKernel((const void*)&probe_placement, dim3(grid), dim3(kPlacementBlock),
+                                pargs, 0, static_cast<hipStream_t>(stream));
+  }
   if ((kind != 2 && nsrc < 1) || (kind != 1 && ndst < 1)) return -1;
   ProbeArgs a{};
   for (int k = 0; k < nsrc; ++k) {

@@ -21,13 +21,91 @@ The GEMM is a plain library GEMM (``torch.mm``: hipBLASLt/rocBLAS), which
 writes the rank's partial P_0 in place; partials 1..N-1 stand for the peers'
 and are already resident.  The fused kernels are this library's.  Both
 streams keep the default priority.
+
+The pages give the fused kernel a few SMs and leave the GEMM the rest ([Blog],
+"Fix two": the kernel saturates the link on a small fraction of the SMs).
+``MaskedStream`` is the MI355X tool for that partition: a HIP stream whose
+kernels may only run on a chosen set of CUs (``hipExtStreamCreateWithCUMask``).
 """
 
 from __future__ import annotations
 
-from typing import Optional
+import ctypes
+from typing import Optional, Sequence
 
 import torch
+
+NUM_MASK_BITS = 256
+
+
+def _hip_runtime() -> ctypes.CDLL:
+    # torch has already loaded the HIP runtime under this soname; dlopen returns
+    # that same instance, so streams made here are usable by torch and by this
+    # library's launches.
+    torch.cuda.init()
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    hip.hipExtStreamCreateWithCUMask.restype = ctypes.c_int
+    hip.hipExtStreamGetCUMask.argtypes = [ctypes.c_void_p, ctypes.c_uint32,
+                                          ctypes.POINTER(ctypes.c_uint32)]
+    hip.hipExtStreamGetCUMask.restype = ctypes.c_int
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipStreamDestroy.restype = ctypes.c_int
+    return hip
+
+
+def mask_words(bits: Sequence[int], num_bits: int = NUM_MASK_BITS) -> list:
+    """CU-mask bit indices -> the 32-bit words ``hipExtStreamCreateWithCUMask``
+    takes (bit b is bit b % 32 of word b // 32)."""
+    words = [0] * ((num_bits + 31) // 32)
+    for b in bits:
+        if not 0 <= b < num_bits:
+            raise ValueError(f"CU mask bit {b} outside [0, {num_bits})")
+        words[b // 32] |= 1 << (b % 32)
+    return words
+
+
+class MaskedStream:
+    """A HIP stream (default priority) restricted to the CUs whose mask bits
+    are given, wrapped as a torch stream (``.stream``).  ``close()`` waits for
+    the stream's work and destroys it."""
+
+    def __init__(self, bits: Sequence[int], num_bits: int = NUM_MASK_BITS):
+        bits = sorted(set(bits))
+        if not bits:
+            raise ValueError("a CU mask needs at least one CU")
+        self.bits = bits
+        self._hip = _hip_runtime()
+        words = mask_words(bits, num_bits)
+        arr = (ctypes.c_uint32 * len(words))(*words)
+        handle = ctypes.c_void_p()
+        rc = self._hip.hipExtStreamCreateWithCUMask(ctypes.byref(handle), len(words), arr)
+        if rc != 0:
+            raise RuntimeError(f"hipExtStreamCreateWithCUMask failed with HIP error {rc}")
+        self._handle = handle.value
+        self.stream = torch.cuda.ExternalStream(self._handle)
+
+    def mask(self) -> list:
+        """The mask as the runtime holds it (32-bit words)."""
+        n = (NUM_MASK_BITS + 31) // 32
+        arr = (ctypes.c_uint32 * n)()
+        rc = self._hip.hipExtStreamGetCUMask(self._handle, n, arr)
+        if rc != 0:
+            raise RuntimeError(f"hipExtStreamGetCUMask failed with HIP error {rc}")
+        return list(arr)
+
+    def close(self):
+        if self._handle is not None:
+            self.stream.synchronize()
+            self._hip.hipStreamDestroy(self._handle)
+            self._handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
 
 from ._lib import tw_fused_reduce_rmsnorm, tw_fused_reduce_rmsnorm_grid
 

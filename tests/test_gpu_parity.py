@@ -404,3 +404,22 @@ def test_nan_input_propagates_to_its_row_only():
     y, x, _ = _oracle(d, rows=keep)
     check(out[keep], y, "bf16", "out")
     check(rout[keep], x, "bf16", "residual_out")
+
+
+@pytest.mark.parametrize("num_cus", [8, 64, 256])
+def test_cu_masked_stream_gives_identical_results(num_cus):
+    # The first k mask bits spread k CUs evenly over the XCDs (bit b belongs to
+    # XCD b mod 8).  Where the workgroups run must not change a single bit.
+    from reduce_rmsnorm_amd.overlap import MaskedStream, mask_words
+    d = make_inputs("llama70b", num_tokens=200, hidden=8192, seed=7)
+    parts, res, w = upload(d)
+    ref_out, ref_rout = _run_full(parts, res, w, d["eps"])
+    say(f"fused launch on a stream masked to {num_cus} CUs")
+    with MaskedStream(range(num_cus)) as ms:
+        assert ms.mask() == mask_words(range(num_cus))
+        out = torch.full_like(res, float("nan"))
+        rout = torch.full_like(res, float("nan"))
+        tw.PreparedFused(parts, res, w, d["eps"], out, rout, ms.stream)()
+        ms.stream.synchronize()
+    np.testing.assert_array_equal(to_host(out), ref_out)
+    np.testing.assert_array_equal(to_host(rout), ref_rout)
