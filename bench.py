@@ -124,6 +124,16 @@ def run_ceiling(sets, R, rows, h, itemsize, stream, steps, timer):
 OVERLAP_K = 3584
 
 
+def rotation_sets(rows, hidden, num_partials, itemsize) -> int:
+    """Buffer sets to rotate so that the inputs, and the outputs on their own,
+    of the sets touched between two uses of one set each exceed twice the
+    MALL (at most MAX_ROTATE)."""
+    in_bytes = (num_partials + 1) * rows * hidden * itemsize
+    out_bytes = 2 * rows * hidden * itemsize
+    return min(MAX_ROTATE, max(math.ceil(2 * MALL_BYTES / (in_bytes + out_bytes)) + 1,
+                               math.ceil(2 * MALL_BYTES / out_bytes) + 1))
+
+
 def _on(stream, fn, i):
     import torch
     with torch.cuda.stream(stream):
@@ -140,14 +150,15 @@ def run_overlap(tw, torch, wl, plan_kw) -> list:
     stream_b = torch.cuda.Stream()
     rows = []
     for T in (1024, 2048, 4096, 8192):
-        step = LayerStep(T, wl.hidden, OVERLAP_K, wl.num_partials, eps=wl.eps, sets=2)
+        nsets = rotation_sets(T, wl.hidden, wl.num_partials, 2)
+        step = LayerStep(T, wl.hidden, OVERLAP_K, wl.num_partials, eps=wl.eps, sets=nsets)
         iters = max(20, int(4e-3 / (T * 4e-9 + 1e-6)))
 
         def measure(fn):
             # Eager first: it also lets the GEMM library finish its lazy per-shape
             # set-up, which it may not do while a stream is being captured.
             e_us = time_steps(fn, stream_a, stream_b, max(10, iters // 4))
-            graphs = [capture(fn, stream_a, stream_b, i) for i in range(2)]
+            graphs = [capture(fn, stream_a, stream_b, i) for i in range(nsets)]
             g_us = time_graphs(graphs, stream_a, iters)
             del graphs
             return g_us, e_us
@@ -304,7 +315,8 @@ def run_cu_mask(tw, torch, wl, sets, R, w, step_bytes) -> dict:
     rows = []
     default_a, default_b = torch.cuda.Stream(), torch.cuda.Stream()
     for T in (4096, 8192):
-        step = LayerStep(T, wl.hidden, OVERLAP_K, wl.num_partials, eps=wl.eps, sets=2)
+        step = LayerStep(T, wl.hidden, OVERLAP_K, wl.num_partials, eps=wl.eps,
+                         sets=rotation_sets(T, wl.hidden, wl.num_partials, 2))
         P = T // 2
         iters = 40
         base = time_steps(lambda i: step.run_unsplit(i, default_a), default_a, default_b, iters)
@@ -402,9 +414,7 @@ def main():
     # nor the outputs of the sets fit in the memory-side cache: output buffers
     # that stay resident there would absorb their writes, which on the
     # 1024-row headline shape makes a launch look about 1.6% faster.
-    out_bytes = 2 * rows * h * (2 if wl.dtype == "bf16" else 4)
-    R = args.rotate or min(MAX_ROTATE, max(math.ceil(2 * MALL_BYTES / step_bytes) + 1,
-                                           math.ceil(2 * MALL_BYTES / out_bytes) + 1))
+    R = args.rotate or rotation_sets(rows, h, N, 2 if wl.dtype == "bf16" else 4)
 
     base_parts, base_res, w = up(d["partials"]), up(d["residual"]), up(d["weight"])
     sets = []
