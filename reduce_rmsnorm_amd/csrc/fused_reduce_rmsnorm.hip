@@ -258,13 +258,21 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
   hipError_t e;
   if (L.max_workgroups <= 0 || L.max_workgroups >= L.num_rows) {
     const KernelFn fn = bf16 ? kTableBF16[g][L.num_partials - 1] : kTableF32[g][L.num_partials - 1];
-    void* args[] = {&k};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)L.num_rows),
-                        dim3(block), args, 0, static_cast<hipStream_t>(L.stream));
+    const int64_t chunk = max_rows_per_dispatch(block);
+    e = hipSuccess;
+    for (int64_t r0 = 0; r0 < L.num_rows && e == hipSuccess; r0 += chunk) {
+      const int64_t n = L.num_rows - r0 < chunk ? L.num_rows - r0 : chunk;
+      k.row_begin = L.row_begin + r0;
+      void* args[] = {&k};
+      e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)n), dim3(block), args,
+                          0, static_cast<hipStream_t>(L.stream));
+    }
   } else {
     const RowsKernelFn fn =
         bf16 ? kRowsTableBF16[g][L.num_partials - 1] : kRowsTableF32[g][L.num_partials - 1];
-    int64_t rows_per_wg = (L.num_rows + L.max_workgroups - 1) / L.max_workgroups;
+    const int64_t cap = max_rows_per_dispatch(block);
+    const int64_t wgs = L.max_workgroups < cap ? L.max_workgroups : cap;
+    int64_t rows_per_wg = (L.num_rows + wgs - 1) / wgs;
     int64_t row_end = L.row_begin + L.num_rows;
     const unsigned grid = (unsigned)((L.num_rows + rows_per_wg - 1) / rows_per_wg);
     void* args[] = {&k, &rows_per_wg, &row_end};

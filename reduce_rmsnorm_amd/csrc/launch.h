@@ -9,6 +9,16 @@ namespace tw {
 
 constexpr int kMaxPartials = 16;
 
+// The most work-items one dispatch carries.  The dispatch packet holds the
+// grid size in work-items as a 32-bit field; staying below 2^31 also keeps
+// every count a non-negative int.  Launches over more rows than
+// kMaxLaunchWorkItems / block are split into several dispatches over
+// consecutive row ranges (one-workgroup-per-row kernels), or have their
+// workgroup count capped (consecutive-rows kernel).  The per-row code is the
+// same either way, so the results do not change.
+constexpr int64_t kMaxLaunchWorkItems = 0x7FFFFFFF;
+inline int64_t max_rows_per_dispatch(int block) { return kMaxLaunchWorkItems / block; }
+
 struct FusedLaunch {
   const void* partials[kMaxPartials];
   int32_t num_partials;

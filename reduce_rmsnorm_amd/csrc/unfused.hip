@@ -201,10 +201,19 @@ int launch_reduce(const ReduceLaunch& L, char* err, size_t errlen) {
   k.reduced = static_cast<u32x4*>(L.reduced);
   k.nvec = (int32_t)nvec;
   const ReduceFn fn = bf16 ? kReduceBF16[g][L.num_partials - 1] : kReduceF32[g][L.num_partials - 1];
-  void* args[] = {&k};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)L.num_rows),
-                                       dim3(kGeometry[g].block), args, 0,
-                                       static_cast<hipStream_t>(L.stream));
+  // Row ranges of at most max_rows_per_dispatch rows, each its own dispatch
+  // with the tensors' base pointers advanced to the range's first row.
+  const int64_t chunk = max_rows_per_dispatch(kGeometry[g].block);
+  hipError_t e = hipSuccess;
+  for (int64_t r0 = 0; r0 < L.num_rows && e == hipSuccess; r0 += chunk) {
+    const int64_t n = L.num_rows - r0 < chunk ? L.num_rows - r0 : chunk;
+    ReduceArgs kc = k;
+    for (int i = 0; i < L.num_partials; ++i) kc.partials[i] = k.partials[i] + r0 * nvec;
+    kc.reduced = k.reduced + r0 * nvec;
+    void* args[] = {&kc};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)n),
+                        dim3(kGeometry[g].block), args, 0, static_cast<hipStream_t>(L.stream));
+  }
   if (e != hipSuccess) {
     std::snprintf(err, errlen, "hipLaunchKernel: %s", hipGetErrorString(e));
     return (int)e;
@@ -227,10 +236,19 @@ int launch_add_rmsnorm(const AddNormLaunch& L, char* err, size_t errlen) {
   k.hidden = (float)L.hidden;
   k.eps = L.eps;
   const AddNormFn fn = bf16 ? kAddNormBF16[g] : kAddNormF32[g];
-  void* args[] = {&k};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)L.num_rows),
-                                       dim3(kGeometry[g].block), args, 0,
-                                       static_cast<hipStream_t>(L.stream));
+  const int64_t chunk = max_rows_per_dispatch(kGeometry[g].block);
+  hipError_t e = hipSuccess;
+  for (int64_t r0 = 0; r0 < L.num_rows && e == hipSuccess; r0 += chunk) {
+    const int64_t n = L.num_rows - r0 < chunk ? L.num_rows - r0 : chunk;
+    AddNormArgs kc = k;
+    kc.input = k.input + r0 * nvec;
+    kc.residual = k.residual + r0 * nvec;
+    kc.out = k.out + r0 * nvec;
+    kc.residual_out = k.residual_out + r0 * nvec;
+    void* args[] = {&kc};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)n),
+                        dim3(kGeometry[g].block), args, 0, static_cast<hipStream_t>(L.stream));
+  }
   if (e != hipSuccess) {
     std::snprintf(err, errlen, "hipLaunchKernel: %s", hipGetErrorString(e));
     return (int)e;

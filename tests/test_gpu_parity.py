@@ -423,3 +423,43 @@ def test_cu_masked_stream_gives_identical_results(num_cus):
         ms.stream.synchronize()
     np.testing.assert_array_equal(to_host(out), ref_out)
     np.testing.assert_array_equal(to_host(rout), ref_rout)
+
+
+def test_row_count_beyond_one_dispatch():
+    # 70 M rows of 8 bf16 elements run 64-thread workgroups: 4.5e9 work-items,
+    # more than one dispatch carries (below 2^31).  One workgroup per row
+    # then takes three dispatches over consecutive row ranges; the
+    # consecutive-rows kernel asked for 69 M workgroups (35 M of them holding
+    # two rows, 2.2e9 work-items) is capped to 33.5 M workgroups of three
+    # rows.  Every row must still be computed, once, with the same bits.
+    T, h, N = 70_000_000, 8, 2
+    chunk = (2 ** 31 - 1) // 64
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    parts = (torch.randn(N, T, h, device="cuda", generator=g, dtype=torch.bfloat16) * 0.5)
+    res = torch.randn(T, h, device="cuda", generator=g, dtype=torch.bfloat16)
+    w = (1 + 0.05 * torch.randn(h, device="cuda", generator=g)).to(torch.bfloat16)
+    eps = 1e-5
+    say(f"fused, T={T} h={h} N={N}: more rows than one dispatch holds")
+    out, rout = tw.tw_fused_reduce_rmsnorm(parts, res, w, eps)
+    say("grid launch asking for 69 M workgroups")
+    out_g, rout_g = tw.tw_fused_reduce_rmsnorm_grid(parts, res, w, eps, 69_000_000)
+    torch.cuda.synchronize()
+    assert torch.equal(out_g, out) and torch.equal(rout_g, rout)
+    del out_g, rout_g
+    say("unfused comparator on the same rows")
+    out_u, rout_u, _ = tw.tw_unfused_reduce_rmsnorm(parts, res, w, eps)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    idx = np.unique(np.concatenate([
+        np.arange(4), np.arange(chunk - 3, chunk + 3), np.arange(2 * chunk - 3, 2 * chunk + 3),
+        np.arange(T - 4, T), rng.integers(0, T, 4000)]))
+    ti = torch.from_numpy(idx).to("cuda")
+    p_host = [to_host(parts[i].index_select(0, ti)) for i in range(N)]
+    r_host = to_host(res.index_select(0, ti))
+    y, x, _ = oracle.fused_reduce_rmsnorm(p_host, r_host, to_host(w), eps, "bf16")
+    check(to_host(out.index_select(0, ti)), y, "bf16", "out")
+    check(to_host(rout.index_select(0, ti)), x, "bf16", "residual_out")
+    yu, xu, _ = oracle.unfused_reduce_rmsnorm(p_host, r_host, to_host(w), eps, "bf16")
+    check(to_host(out_u.index_select(0, ti)), yu, "bf16", "unfused out")
+    check(to_host(rout_u.index_select(0, ti)), xu, "bf16", "unfused residual_out")
