@@ -52,7 +52,7 @@ typedef enum {
 #define TW_MAX_PARTIALS 16        /* tensor-parallel degree N handled */
 #define TW_MAX_ROW_BYTES 131072   /* largest hidden * sizeof(dtype): h <= 65536
                                      for bf16, h <= 32768 for fp32 */
-#define TW_MAX_TOKENS 2147483647  /* largest num_tokens (one workgroup per row) */
+#define TW_MAX_TOKENS 2147483647  /* largest num_tokens */
 
 #define TW_ABI_VERSION 1
 
@@ -85,6 +85,9 @@ void tw_set_pointer_checks(int32_t enabled);
  * ranks (on the pages the NVSwitch reduces them; here they are N buffers in
  * this GPU's memory).  The partial sum is a compensated (error-free
  * transformation) float32 sum; rounding to bf16 is round-to-nearest-even.
+ * NaN and infinite inputs propagate to their row.  A row whose sum of
+ * squares overflows float32 (|x| above about 1.8e19) gets rs = 0 and out = 0
+ * (NaN where x is infinite); residual_out is still x rounded.
  *
  * Arguments
  *   partials      host array of num_partials device pointers, each to a

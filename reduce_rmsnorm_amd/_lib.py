@@ -133,6 +133,8 @@ def _marshal(partials, residual, weight, out, residual_out):
     for t in parts + [residual, weight]:
         if not t.is_cuda:
             raise ValueError("every tensor must be on a GPU (there is no CPU path)")
+        if t.device != residual.device:
+            raise ValueError("every tensor must be on the residual's GPU")
         if t.dtype != residual.dtype:
             raise ValueError("every tensor must share one dtype")
         if not t.is_contiguous():
@@ -156,6 +158,8 @@ def _marshal(partials, residual, weight, out, residual_out):
 
 def _stream_handle(device: torch.device, stream: Optional[torch.cuda.Stream]):
     s = stream if stream is not None else torch.cuda.current_stream(device)
+    if s.device != device:
+        raise ValueError(f"the stream belongs to {s.device}, the tensors to {device}")
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -320,7 +324,7 @@ class PreparedFused:
         lib = load_library()
         parts, ptrs, T, h, out, residual_out = _marshal(partials, residual, weight, out,
                                                         residual_out)
-        self._keep = (parts, residual, weight, out, residual_out, ptrs)
+        self._keep = (parts, residual, weight, out, residual_out, ptrs, stream)
         self.out, self.residual_out = out, residual_out
         head = (ptrs, len(parts), residual.data_ptr(), weight.data_ptr(), out.data_ptr(),
                 residual_out.data_ptr(), T, h, ctypes.c_float(float(eps)), _dtype_code(residual))

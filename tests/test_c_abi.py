@@ -1,0 +1,77 @@
+"""The C ABI from plain C: tests/c/abi_check.c is compiled as C99 (and, to
+check the header's C++ guards, as C++11) against include/tokenweave.h and
+linked with the built library.  Its planner results must match the oracle
+field for field, and its argument checks must return the documented status
+codes.  No device work: runs without a GPU."""
+
+import os
+import random
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+from reduce_rmsnorm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "tests", "c", "abi_check.c")
+FIELDS = ("prefix_tokens", "suffix_tokens", "offset", "waves_unsplit", "waves_prefix",
+          "waves_suffix", "reason")
+
+# status codes the header documents for each case abi_check.c runs
+EXPECTED_STATUS = {
+    "null_partials": _lib.TW_ERR_INVALID_ARG,
+    "hidden_not_16_bytes": _lib.TW_ERR_UNSUPPORTED,
+    "negative_eps": _lib.TW_ERR_INVALID_ARG,
+    "shard_index_out_of_range": _lib.TW_ERR_INVALID_ARG,
+    "out_overlaps_partial": _lib.TW_ERR_INVALID_ARG,
+    "empty_batch": _lib.TW_OK,
+    "plan_null_problem": _lib.TW_ERR_INVALID_ARG,
+    "plan_zero_tile": _lib.TW_ERR_INVALID_ARG,
+}
+
+
+def _build(tmp_path, compiler, std, lang):
+    exe = str(tmp_path / f"abi_check_{lang}")
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    cmd = [compiler, f"-std={std}", "-Wall", "-Wextra", "-Werror", "-pedantic", "-x", lang, SRC,
+           "-x", "none", "-I", os.path.join(ROOT, "include"), "-L", libdir, "-ltokenweave",
+           f"-Wl,-rpath,{libdir}", "-o", exe]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    return exe
+
+
+@pytest.fixture(scope="module")
+def cases():
+    rnd = random.Random(5)
+    c = [(257, 1, 1, 256, 1, 0), (514, 1, 1, 256, 1, 0), (300, 1, 1, 132, 1, 0),
+         (393, 1, 1, 132, 1, 0), (0, 1, 1, 256, 1, 0), (100, 1, 1, 256, 1, 1024),
+         (4096, 256, 32, 256, 1, 1024), (8192, 256, 16, 256, 1, 4096)]
+    for _ in range(300):
+        c.append((rnd.randint(0, 70000), rnd.choice([1, 64, 128, 256]), rnd.randint(1, 64),
+                  rnd.choice([132, 256, 304]), rnd.randint(1, 4), rnd.choice([0, 1024, 4096])))
+    return c
+
+
+@pytest.mark.parametrize("compiler,std,lang", [("gcc", "c99", "c"), ("g++", "c++11", "c++")])
+def test_c_program_matches_oracle(tmp_path, cases, compiler, std, lang):
+    if shutil.which(compiler) is None:
+        pytest.skip(f"{compiler} not installed")
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail(f"{_lib.LIB_PATH} is missing: build it first")
+    exe = _build(tmp_path, compiler, std, lang)
+    stdin = "".join(" ".join(str(v) for v in c) + "\n" for c in cases)
+    run = subprocess.run([exe], input=stdin, capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stderr
+    lines = run.stdout.splitlines()
+    assert lines[-1] == "done"
+    for c, ln in zip(cases, lines[:len(cases)]):
+        got = [int(v) for v in ln.split()]
+        assert got[0] == _lib.TW_OK, (c, ln)
+        T, tpc, tiles, cus, occ, thr = c
+        want = oracle.split_plan(T, tokens_per_cta=tpc, ctas_per_token_tile=tiles, num_cus=cus,
+                                 ctas_per_cu=occ, min_split_tokens=thr)
+        assert got[1:] == [want[f] for f in FIELDS], (c, got, want)
+    checks = dict(ln.split() for ln in lines[len(cases):-1])
+    assert {k: int(v) for k, v in checks.items()} == EXPECTED_STATUS

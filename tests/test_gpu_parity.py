@@ -463,3 +463,50 @@ def test_row_count_beyond_one_dispatch():
     yu, xu, _ = oracle.unfused_reduce_rmsnorm(p_host, r_host, to_host(w), eps, "bf16")
     check(to_host(out_u.index_select(0, ti)), yu, "bf16", "unfused out")
     check(to_host(rout_u.index_select(0, ti)), xu, "bf16", "unfused residual_out")
+
+
+def test_binding_rejects_mismatched_tensors():
+    d = make_inputs("llama70b", num_tokens=8, hidden=256)
+    parts, res, w = upload(d)
+    say("binding argument checks")
+    bad = [
+        (lambda: tw.tw_fused_reduce_rmsnorm(parts, res.float(), w, 1e-5), "dtype"),
+        (lambda: tw.tw_fused_reduce_rmsnorm(parts[:, :4], res, w, 1e-5), "shape"),
+        (lambda: tw.tw_fused_reduce_rmsnorm(parts, res, w[:128], 1e-5), "weight"),
+        (lambda: tw.tw_fused_reduce_rmsnorm(parts, res.t().contiguous().t(), w, 1e-5),
+         "contiguous"),
+        (lambda: tw.tw_fused_reduce_rmsnorm(parts, res, w, 1e-5, out=torch.empty(8, 128, dtype=res.dtype,
+                                                                                  device="cuda")),
+         "out"),
+        (lambda: tw.tw_fused_reduce_rmsnorm(parts, res, w.cpu(), 1e-5), "GPU"),
+        (lambda: tw.PreparedFused(parts, res, w, 1e-5, torch.empty_like(res),
+                                  torch.empty_like(res), mode="rows"), "mode"),
+    ]
+    for fn, needle in bad:
+        with pytest.raises(ValueError, match=needle):
+            fn()
+    # Errors the library itself finds come back as TokenWeaveError with its text.
+    with pytest.raises(tw.TokenWeaveError, match="eps"):
+        tw.tw_fused_reduce_rmsnorm(parts, res, w, float("nan"))
+    with pytest.raises(tw.TokenWeaveError, match="shard_index"):
+        tw.tw_shard_rmsnorm(parts, res, w, 1e-5, shard_index=len(parts))
+
+
+def test_row_whose_sum_of_squares_overflows_float32():
+    # x = 2^70 in every element: x^2 = 2^140 overflows float32, so rs = 0 and
+    # the documented result is out = 0 for that row, residual_out = x exactly.
+    # The neighbouring rows are untouched by it.
+    d = make_inputs("llama70b", num_tokens=3, hidden=512)
+    big = np.uint16(0x6280)          # bf16 bits of 2^70
+    d["partials"][:, 1, :] = 0
+    d["partials"][0, 1, :] = big
+    d["residual"][1, :] = 0
+    parts, res, w = upload(d)
+    say("row with x = 2^70: float32 sum of squares overflows")
+    out, rout = _run_full(parts, res, w, d["eps"])
+    assert oracle.bf16_bits_to_f64(np.array([big]))[0] == 2.0 ** 70
+    assert (out[1] & 0x7FFF == 0).all(), "out of the overflowing row must be +-0"
+    np.testing.assert_array_equal(rout[1], np.full(512, big))
+    y, x, _ = _oracle(d, rows=[0, 2])
+    check(out[[0, 2]], y, "bf16", "out, other rows")
+    check(rout[[0, 2]], x, "bf16", "residual_out, other rows")
