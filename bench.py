@@ -28,6 +28,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -76,6 +77,10 @@ def parse():
     ap.add_argument("--split-table", action="store_true",
                     help="also time the fused step alone as two launches (prefix, suffix) for "
                          "every offset, next to one launch over all rows")
+    ap.add_argument("--gemm-staircase", action="store_true",
+                    help="also time the layer's row-parallel GEMM alone for M = 64 .. 8192 "
+                         "rows in steps of 64: where its time steps up shows the GEMM's "
+                         "row tile and waves, which the split planner models")
     ap.add_argument("--cu-mask", action="store_true",
                     help="also run the fused kernel on CU-masked streams: where mask bits land "
                          "(XCD, CU), GB/s against the number of CUs, and the split layer step "
@@ -122,6 +127,77 @@ def run_ceiling(sets, R, rows, h, itemsize, stream, steps, timer):
 # Down-projection of a Llama-3-70B-shaped layer under 8-way tensor
 # parallelism: intermediate 28672 / 8 = 3584 columns per rank.
 OVERLAP_K = 3584
+
+
+def run_gemm_staircase(tw, torch, wl, plan_kw) -> dict:
+    """Time X[M, K] @ W[K, h] (bf16, ``torch.mm`` into a preallocated output,
+    the layer GEMM of the overlap step) for M = 64 .. 8192 in steps of 64,
+    each as the mean of graph replays of 20 back-to-back GEMMs (no host launch
+    cost).  Jumps in time against M show the row tile the library picked and
+    where a new wave of tiles starts; the split planner's CTA model
+    (tokens_per_cta x ctas_per_token_tile on 256 CUs) is checked against
+    them."""
+    K, h = OVERLAP_K, wl.hidden
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    x = (torch.randn(8192, K, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+    w = (torch.randn(K, h, device="cuda", generator=g) / K ** 0.5).to(torch.bfloat16)
+    y = torch.empty(8192, h, device="cuda", dtype=torch.bfloat16)
+    side = torch.cuda.Stream()
+    points = []
+    for M in range(64, 8193, 64):
+        with torch.cuda.stream(side):
+            torch.mm(x[:M], w, out=y[:M])       # eager first: the library's per-shape set-up
+        side.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(20):
+                torch.mm(x[:M], w, out=y[:M])
+        with torch.cuda.stream(side):
+            graph.replay()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(side)
+            for _ in range(5):
+                graph.replay()
+            e1.record(side)
+        side.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 100
+        points.append({"m": M, "us": round(us, 2),
+                       "tflops": round(2 * M * K * h / (us * 1e-6) / 1e12, 1)})
+        del graph
+    # A "step" is a rise of more than 8% of the previous time between two
+    # neighbouring M values.
+    steps = [p["m"] for q, p in zip(points, points[1:]) if p["us"] > 1.08 * q["us"]]
+    print("[bench] gemm staircase (M: us): " + ", ".join(f"{p['m']}: {p['us']}" for p in points),
+          file=sys.stderr, flush=True)
+    print(f"[bench] gemm staircase: time rises by >8% at M = {steps}", file=sys.stderr, flush=True)
+    # The pages' offline table from these GEMM times: for each token count,
+    # the offset whose two GEMMs cost least relative to one GEMM over all
+    # rows, next to the analytic planner's choice.
+    t = {p["m"]: p["us"] for p in points}
+    table = []
+    for T in range(1024, 8193, 128):
+        half = T // 2
+        cost = {off: (t[half + off] + t[T - half - off]) / t[T] - 1
+                for off in (0, 64, 128, 192, 256, 512) if off < half}
+        best = min(cost, key=cost.get)
+        plan = tw.tw_split_plan(T, **plan_kw)
+        table.append({"tokens": T, "gemm_us": t[T], "best_offset": best,
+                      "best_penalty": round(cost[best], 4), "planner_reason": plan["reason"],
+                      "planner_offset": plan["offset"],
+                      "planner_penalty": round(cost[plan["offset"]], 4)
+                      if plan["reason"] == 0 else None})
+    split = [e for e in table if e["planner_reason"] == 0]
+    summary = {"planner_splits": len(split),
+               "planner_picks_best": sum(e["planner_offset"] == e["best_offset"] for e in split),
+               "planner_penalty_median": round(statistics.median(e["planner_penalty"] for e in split), 4),
+               "planner_penalty_max": round(max(e["planner_penalty"] for e in split), 4),
+               "best_penalty_median": round(statistics.median(e["best_penalty"] for e in split), 4),
+               "best_penalty_max": round(max(e["best_penalty"] for e in split), 4)}
+    print(f"[bench] gemm split table vs planner: {summary}", file=sys.stderr, flush=True)
+    return {"k": K, "n": h, "points": points, "rises_at": steps, "split_table": table,
+            "summary": summary}
 
 
 def rotation_sets(rows, hidden, num_partials, itemsize) -> int:
@@ -533,6 +609,10 @@ def main():
             print(f"[bench] footprint {G:5d} workgroups: {g_us:9.2f} us  {gbs_g:7.1f} GB/s",
                   file=sys.stderr, flush=True)
 
+    staircase = None
+    if args.gemm_staircase:
+        staircase = run_gemm_staircase(tw, torch, wl, plan_kw)
+
     cu_mask = None
     if args.cu_mask and args.mode == "full":
         cu_mask = run_cu_mask(tw, torch, wl, sets, R, w, step_bytes)
@@ -632,6 +712,8 @@ def main():
         result["split_table"] = split_table
     if cu_mask is not None:
         result["cu_mask"] = cu_mask
+    if staircase is not None:
+        result["gemm_staircase"] = staircase
     if ceiling is not None:
         result["ceiling"] = ceiling
     if args.cpu_seconds > 0:
