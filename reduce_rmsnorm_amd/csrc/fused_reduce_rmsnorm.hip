@@ -18,11 +18,14 @@
 //  * One workgroup per token row.  Each thread owns VPT 16-byte vectors of the
 //    row (vector v = tid + j*BLOCK), so every load and store instruction of a
 //    wave covers 1 KiB of contiguous memory.
-//  * All (N+1)*VPT loads of a thread are issued before the first use (wide
-//    rows with more than two vectors per thread issue them one vector slot
-//    at a time); out of range vectors (h not a multiple of BLOCK*VPT*elems)
-//    load a clamped, valid address and contribute zero, so no branch splits
-//    the load batch.
+//  * With few partials all (N+1)*VPT loads of a thread are issued before
+//    the first use (wide rows issue them a few vector slots at a time).  With
+//    five or more partials on rows of 512-1024 vectors the tensors are loaded
+//    in summation order with one or two in flight per thread: fewer DRAM
+//    regions are open across the chip at a time, and the stream is faster.
+//    Out of range vectors (h not a multiple of BLOCK*VPT*elems) load a
+//    clamped, valid address and contribute zero, so no branch splits a load
+//    batch.
 //  * The partials and the residual are summed with an error-free
 //    transformation (TwoSum) into a float32 pair (s, c); x = s + c.  For bf16
 //    the stored residual is rounded to odd in float32 first and then to bf16
@@ -65,11 +68,41 @@ struct KArgs {
   float eps;
 };
 
+// Tensor I of the summation: partial I for I < N, the residual for I == N.
+#define TW_TENSOR(I) ((I) < N ? a.partials[(I) < N ? (I) : 0] : a.residual)
+
+// Finishing one vector slot J from its compensated pair (S, C): x, the stored
+// residual (correctly rounded for bf16) and the slot's share of the sum of
+// squares, added in slot order.
+#define TW_FINISH_SLOT(J, S, C)                                                        \
+  {                                                                                    \
+    float keep[E];                                                                     \
+_Pragma("unroll")                                                                      \
+    for (int e = 0; e < E; ++e) {                                                      \
+      const float xe = (S)[e] + (C)[e];                                                \
+      x[J][e] = valid[J] ? xe : 0.0f;                                                  \
+      keep[e] = BF16 ? round_to_odd((S)[e], (C)[e], xe) : xe;                          \
+    }                                                                                  \
+    if (valid[J])                                                                      \
+      __builtin_nontemporal_store(pack<BF16>(keep), a.residual_out + base + vi[J]);    \
+_Pragma("unroll")                                                                      \
+    for (int e = 0; e < E; ++e) ss = __builtin_fmaf(x[J][e], x[J][e], ss);             \
+  }
+
 // The per-row body of both fused kernels: everything the fused step does to
 // the row ROW_EXPR, by one workgroup, with the wave partial sums in the LDS
 // array wave_part[BLOCK / 64] and E, NW in scope.  Written once and expanded
 // into each kernel, so that both compile it in a kernel's own context (an
 // inlined device function allocated registers differently and spilled).
+//
+// Two load orders, chosen by the geometry and giving the same arithmetic:
+//  * SEQ == 0: the N+1 loads of CHUNK vector slots are issued together.  With
+//    CHUNK == VPT every load of the row is in flight before the first use;
+//    wide rows take CHUNK slots at a time so their values fit in registers.
+//  * SEQ == D > 0: the tensors are loaded in summation order, D of them in
+//    flight: tensor i + D is requested once tensor i has been added.  Fewer
+//    DRAM regions are open at a time across the chip, which streams faster
+//    when there are many partials.
 #define TW_FUSED_ROW_BODY(ROW_EXPR)                                                    \
   const int tid = threadIdx.x;                                                         \
   const int64_t row = (ROW_EXPR);                                                      \
@@ -85,12 +118,8 @@ _Pragma("unroll")                                                               
     vi[j] = valid[j] ? v : nvec - 1;                                                   \
   }                                                                                    \
                                                                                        \
-  /* Loads are issued CHUNK vector slots at a time: with CHUNK == VPT every */         \
-  /* load of the row is in flight before the first use; wide rows (large VPT) */       \
-  /* take CHUNK slots' N+1 loads at a time so the row's values fit in */               \
-  /* registers.  The arithmetic runs slot by slot in the same order either way. */     \
   u32x4 wraw[VPT];                                                                     \
-  if constexpr (CHUNK == VPT) {                                                        \
+  if constexpr (SEQ > 0 || CHUNK == VPT) {                                             \
 _Pragma("unroll")                                                                      \
     for (int j = 0; j < VPT; ++j) wraw[j] = a.weight[vi[j]];                           \
   }                                                                                    \
@@ -98,45 +127,71 @@ _Pragma("unroll")                                                               
   /* Compensated float32 sum: partials in order, then the residual. */                 \
   float x[VPT][E];                                                                     \
   float ss = 0.0f;                                                                     \
+  if constexpr (SEQ > 0) {                                                             \
+    u32x4 raw[N + 1][VPT];                                                             \
+    float s[VPT][E], c[VPT][E];                                                        \
 _Pragma("unroll")                                                                      \
-  for (int j0 = 0; j0 < VPT; j0 += CHUNK) {                                            \
-    u32x4 raw[N + 1][CHUNK];                                                           \
+    for (int i = 0; i < SEQ && i <= N; ++i)                                            \
 _Pragma("unroll")                                                                      \
-    for (int i = 0; i < N; ++i)                                                        \
+      for (int j = 0; j < VPT; ++j)                                                    \
+        raw[i][j] = __builtin_nontemporal_load(TW_TENSOR(i) + base + vi[j]);           \
+_Pragma("unroll")                                                                      \
+    for (int i = 0; i <= N; ++i) {                                                     \
+      __builtin_amdgcn_sched_barrier(0);                                               \
+_Pragma("unroll")                                                                      \
+      for (int j = 0; j < VPT; ++j) {                                                  \
+        if (i == 0) {                                                                  \
+          unpack<BF16>(raw[0][j], s[j]);                                               \
+_Pragma("unroll")                                                                      \
+          for (int e = 0; e < E; ++e) c[j][e] = 0.0f;                                  \
+        } else {                                                                       \
+          float t[E];                                                                  \
+          unpack<BF16>(raw[i][j], t);                                                  \
+_Pragma("unroll")                                                                      \
+          for (int e = 0; e < E; ++e) two_sum_into(s[j][e], c[j][e], t[e]);            \
+        }                                                                              \
+      }                                                                                \
+      __builtin_amdgcn_sched_barrier(0);                                               \
+      if (i + SEQ <= N) {                                                              \
+_Pragma("unroll")                                                                      \
+        for (int j = 0; j < VPT; ++j)                                                  \
+          raw[i + SEQ <= N ? i + SEQ : N][j] =                                         \
+              __builtin_nontemporal_load(TW_TENSOR(i + SEQ) + base + vi[j]);           \
+      }                                                                                \
+    }                                                                                  \
+_Pragma("unroll")                                                                      \
+    for (int j = 0; j < VPT; ++j) TW_FINISH_SLOT(j, s[j], c[j])                        \
+  } else {                                                                             \
+_Pragma("unroll")                                                                      \
+    for (int j0 = 0; j0 < VPT; j0 += CHUNK) {                                          \
+      u32x4 raw[N + 1][CHUNK];                                                         \
+_Pragma("unroll")                                                                      \
+      for (int i = 0; i < N; ++i)                                                      \
+_Pragma("unroll")                                                                      \
+        for (int jj = 0; jj < CHUNK; ++jj)                                             \
+          raw[i][jj] = __builtin_nontemporal_load(a.partials[i] + base + vi[j0 + jj]); \
 _Pragma("unroll")                                                                      \
       for (int jj = 0; jj < CHUNK; ++jj)                                               \
-        raw[i][jj] = __builtin_nontemporal_load(a.partials[i] + base + vi[j0 + jj]);   \
+        raw[N][jj] = __builtin_nontemporal_load(a.residual + base + vi[j0 + jj]);      \
 _Pragma("unroll")                                                                      \
-    for (int jj = 0; jj < CHUNK; ++jj)                                                 \
-      raw[N][jj] = __builtin_nontemporal_load(a.residual + base + vi[j0 + jj]);        \
+      for (int jj = 0; jj < CHUNK; ++jj) {                                             \
+        const int j = j0 + jj;                                                         \
+        float s[E], c[E], t[E];                                                        \
+        unpack<BF16>(raw[0][jj], s);                                                   \
 _Pragma("unroll")                                                                      \
-    for (int jj = 0; jj < CHUNK; ++jj) {                                               \
-      const int j = j0 + jj;                                                           \
-      float s[E], c[E], t[E];                                                          \
-      unpack<BF16>(raw[0][jj], s);                                                     \
+        for (int e = 0; e < E; ++e) c[e] = 0.0f;                                       \
 _Pragma("unroll")                                                                      \
-      for (int e = 0; e < E; ++e) c[e] = 0.0f;                                         \
+        for (int i = 1; i <= N; ++i) {                                                 \
+          unpack<BF16>(raw[i][jj], t);                                                 \
 _Pragma("unroll")                                                                      \
-      for (int i = 1; i <= N; ++i) {                                                   \
-        unpack<BF16>(raw[i][jj], t);                                                   \
-_Pragma("unroll")                                                                      \
-        for (int e = 0; e < E; ++e) two_sum_into(s[e], c[e], t[e]);                    \
+          for (int e = 0; e < E; ++e) two_sum_into(s[e], c[e], t[e]);                  \
+        }                                                                              \
+        TW_FINISH_SLOT(j, s, c)                                                        \
       }                                                                                \
-      float keep[E];                                                                   \
-_Pragma("unroll")                                                                      \
-      for (int e = 0; e < E; ++e) {                                                    \
-        const float xe = s[e] + c[e];                                                  \
-        x[j][e] = valid[j] ? xe : 0.0f;                                                \
-        keep[e] = BF16 ? round_to_odd(s[e], c[e], xe) : xe;                            \
-      }                                                                                \
-      if (valid[j])                                                                    \
-        __builtin_nontemporal_store(pack<BF16>(keep), a.residual_out + base + vi[j]);  \
-_Pragma("unroll")                                                                      \
-      for (int e = 0; e < E; ++e) ss = __builtin_fmaf(x[j][e], x[j][e], ss);           \
+      if constexpr (CHUNK < VPT) __builtin_amdgcn_sched_barrier(0);                    \
     }                                                                                  \
-    if constexpr (CHUNK < VPT) __builtin_amdgcn_sched_barrier(0);                      \
   }                                                                                    \
-  if constexpr (CHUNK < VPT) {                                                         \
+  if constexpr (SEQ == 0 && CHUNK < VPT) {                                             \
 _Pragma("unroll")                                                                      \
     for (int j = 0; j < VPT; ++j) wraw[j] = a.weight[vi[j]];                           \
   }                                                                                    \
@@ -160,7 +215,7 @@ _Pragma("unroll")                                                               
   }
 
 // One workgroup per row: the launch grid is the row count.
-template <int N, int BLOCK, int VPT, bool BF16, int WPE, int CHUNK>
+template <int N, int BLOCK, int VPT, bool BF16, int WPE, int CHUNK, int SEQ>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(WPE)))
 void fused_reduce_rmsnorm_kernel(KArgs a) {
   constexpr int E = Elem<BF16>::kPerVec;
@@ -175,7 +230,7 @@ void fused_reduce_rmsnorm_kernel(KArgs a) {
 // A barrier between rows keeps a row's wave partial sums from overwriting the
 // previous row's while a slower wave still reads them.  Few workgroups are
 // launched by design, so no occupancy cap is requested.
-template <int N, int BLOCK, int VPT, bool BF16, int CHUNK>
+template <int N, int BLOCK, int VPT, bool BF16, int CHUNK, int SEQ>
 __global__ __launch_bounds__(BLOCK) void fused_reduce_rmsnorm_rows_kernel(KArgs a,
                                                                           int64_t rows_per_wg,
                                                                           int64_t row_end) {
@@ -193,35 +248,47 @@ __global__ __launch_bounds__(BLOCK) void fused_reduce_rmsnorm_rows_kernel(KArgs 
 using KernelFn = void (*)(KArgs);
 using RowsKernelFn = void (*)(KArgs, int64_t, int64_t);
 
-template <bool BF16, int G, int... Ns>
+// Kernel tables by [row class][N - 1].  SEQ_ORDER selects the geometry's own
+// load order; without it every entry loads all tensors at once (the same
+// arithmetic, for launches too small to fill the CUs).
+constexpr int load_order(int g, int n, bool seq_order) {
+  return seq_order ? fused_geometry(g, n).seq : 0;
+}
+template <bool BF16, bool SEQ_ORDER, int G, int... Ns>
 constexpr std::array<KernelFn, sizeof...(Ns)> row_of(std::integer_sequence<int, Ns...>) {
   return {&fused_reduce_rmsnorm_kernel<Ns + 1, fused_geometry(G, Ns + 1).block,
                                        fused_geometry(G, Ns + 1).vpt, BF16,
                                        fused_geometry(G, Ns + 1).waves_per_eu,
-                                       fused_geometry(G, Ns + 1).chunk>...};
+                                       fused_geometry(G, Ns + 1).chunk,
+                                       load_order(G, Ns + 1, SEQ_ORDER)>...};
 }
-template <bool BF16, int G, int... Ns>
+template <bool BF16, bool SEQ_ORDER, int G, int... Ns>
 constexpr std::array<RowsKernelFn, sizeof...(Ns)> rows_row_of(std::integer_sequence<int, Ns...>) {
   return {&fused_reduce_rmsnorm_rows_kernel<Ns + 1, fused_geometry(G, Ns + 1).block,
                                             fused_geometry(G, Ns + 1).vpt, BF16,
-                                            fused_geometry(G, Ns + 1).chunk>...};
+                                            fused_geometry(G, Ns + 1).chunk,
+                                            load_order(G, Ns + 1, SEQ_ORDER)>...};
 }
 
-template <bool BF16, int... Gs>
+template <bool BF16, bool SEQ_ORDER, int... Gs>
 constexpr std::array<std::array<KernelFn, kMaxPartials>, sizeof...(Gs)> table_of(
     std::integer_sequence<int, Gs...>) {
-  return {row_of<BF16, Gs>(std::make_integer_sequence<int, kMaxPartials>{})...};
+  return {row_of<BF16, SEQ_ORDER, Gs>(std::make_integer_sequence<int, kMaxPartials>{})...};
 }
-template <bool BF16, int... Gs>
+template <bool BF16, bool SEQ_ORDER, int... Gs>
 constexpr std::array<std::array<RowsKernelFn, kMaxPartials>, sizeof...(Gs)> rows_table_of(
     std::integer_sequence<int, Gs...>) {
-  return {rows_row_of<BF16, Gs>(std::make_integer_sequence<int, kMaxPartials>{})...};
+  return {rows_row_of<BF16, SEQ_ORDER, Gs>(std::make_integer_sequence<int, kMaxPartials>{})...};
 }
 
-const auto kTableF32 = table_of<false>(std::make_integer_sequence<int, kNumGeometries>{});
-const auto kTableBF16 = table_of<true>(std::make_integer_sequence<int, kNumGeometries>{});
-const auto kRowsTableF32 = rows_table_of<false>(std::make_integer_sequence<int, kNumGeometries>{});
-const auto kRowsTableBF16 = rows_table_of<true>(std::make_integer_sequence<int, kNumGeometries>{});
+using Geoms = std::make_integer_sequence<int, kNumGeometries>;
+// [bf16][sequenced order]
+const std::array<std::array<std::array<std::array<KernelFn, kMaxPartials>, kNumGeometries>, 2>, 2>
+    kTable = {{{table_of<false, false>(Geoms{}), table_of<false, true>(Geoms{})},
+               {table_of<true, false>(Geoms{}), table_of<true, true>(Geoms{})}}};
+const std::array<std::array<std::array<std::array<RowsKernelFn, kMaxPartials>, kNumGeometries>, 2>, 2>
+    kRowsTable = {{{rows_table_of<false, false>(Geoms{}), rows_table_of<false, true>(Geoms{})},
+                   {rows_table_of<true, false>(Geoms{}), rows_table_of<true, true>(Geoms{})}}};
 
 }  // namespace
 
@@ -254,10 +321,12 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
   k.hidden = (float)L.hidden;
   k.eps = L.eps;
 
-  const int block = fused_geometry(g, L.num_partials).block;
+  const Geometry geo = fused_geometry(g, L.num_partials);
+  const int block = geo.block;
   hipError_t e;
   if (L.max_workgroups <= 0 || L.max_workgroups >= L.num_rows) {
-    const KernelFn fn = bf16 ? kTableBF16[g][L.num_partials - 1] : kTableF32[g][L.num_partials - 1];
+    const bool seq = L.num_rows >= seq_min_workgroups(block);
+    const KernelFn fn = kTable[bf16][seq][g][L.num_partials - 1];
     const int64_t chunk = max_rows_per_dispatch(block);
     e = hipSuccess;
     for (int64_t r0 = 0; r0 < L.num_rows && e == hipSuccess; r0 += chunk) {
@@ -268,10 +337,9 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
                           0, static_cast<hipStream_t>(L.stream));
     }
   } else {
-    const RowsKernelFn fn =
-        bf16 ? kRowsTableBF16[g][L.num_partials - 1] : kRowsTableF32[g][L.num_partials - 1];
     const int64_t cap = max_rows_per_dispatch(block);
     const int64_t wgs = L.max_workgroups < cap ? L.max_workgroups : cap;
+    const RowsKernelFn fn = kRowsTable[bf16][wgs >= seq_min_workgroups(block)][g][L.num_partials - 1];
     int64_t rows_per_wg = (L.num_rows + wgs - 1) / wgs;
     int64_t row_end = L.row_begin + L.num_rows;
     const unsigned grid = (unsigned)((L.num_rows + rows_per_wg - 1) / rows_per_wg);

@@ -13,14 +13,17 @@ struct Geometry {
   int vpt;            // 16-byte vectors per thread
   int waves_per_eu;   // occupancy the compiler must allow (1: no constraint)
   int chunk;          // vector slots whose loads are issued together (divides vpt)
+  int seq;            // 0: all N+1 tensors of a chunk loaded at once; D > 0: the
+                      // tensors are loaded in summation order, D in flight
 };
 
 // (threads per workgroup, vectors per thread) by 16-byte vectors per row: the
 // first entry whose capacity covers the row.  Measured on MI355X at 184-738 MB
-// per launch, N = 8 bf16:
+// per launch, N = 8 bf16, all loads of a row issued at once:
 //  * h = 8192 (1024 vectors): 512 x 2 at 6 waves per SIMD (at most 80 VGPRs,
 //    three workgroups per CU) 31.5 us; uncapped 32.7 us; 1024 x 1 33.4 us;
-//    256 x 4 36.0-36.5 us.
+//    256 x 4 36.0-36.5 us.  (With five or more partials fused_geometry below
+//    replaces this entry.)
 //  * h = 4096 (512 vectors): 512 x 1 at 8 waves per SIMD 122.9-123.2 us
 //    (T = 8192); 256 x 2 128.9 us.
 //  * h = 16384 (2048 vectors): 512 x 4 at 4 waves per SIMD, loads two slots
@@ -28,20 +31,45 @@ struct Geometry {
 // The occupancy cap applies up to N = 8 partials, where it costs no scratch;
 // with more partials the compiler's own allocation is kept.
 constexpr Geometry kGeometry[] = {
-    {64, 1, 1, 1},  {128, 1, 1, 1}, {256, 1, 1, 1},  {512, 1, 8, 1},
-    {512, 2, 6, 2}, {512, 4, 4, 2}, {1024, 4, 1, 1}, {1024, 8, 1, 1}};
+    {64, 1, 1, 1, 0},  {128, 1, 1, 1, 0}, {256, 1, 1, 1, 0},  {512, 1, 8, 1, 0},
+    {512, 2, 6, 2, 0}, {512, 4, 4, 2, 0}, {1024, 4, 1, 1, 0}, {1024, 8, 1, 1, 0}};
 constexpr int kMaxCappedPartials = 8;
 
-// The geometry the fused kernels use for row class g and N partials.  Up to
-// kMaxCappedPartials the table entry applies with its occupancy cap.  Above
-// it the cap is dropped (it would force spills), and the 512 x 2 class runs
-// 1024 x 1 instead: at N = 16, T = 1024, h = 8192 it took 54.8 us (62 VGPRs)
-// against 57.6 us for uncapped 512 x 2.
+// The geometry the fused kernels use for row class g and N partials.
+//
+// Loading the tensors in summation order, with only D of them in flight per
+// thread, keeps fewer DRAM regions open at once than issuing all N+1 loads
+// together, and beats it once there are enough partials.  Measured on MI355X
+// (bf16, inputs and outputs rotated past the MALL):
+//  * 512 x 2 class (h = 8192): 1024 x 1 with D = 1, T = 1024: N = 7 28.3 us
+//    against 29.2; N = 8 30.8 against 31.7; N = 12 40.5 against 44.0; N = 16
+//    50.3 against 55.3 (T = 4096, N = 8: 117.5 against 123.2).  N = 5, 6 do
+//    best with D = 2 (23.2 against 23.9 us, 25.9 against 26.9); for N <= 4
+//    loading everything at once stays best (N = 2: 16.0 against 16.6 us).
+//  * 512 x 1 class (h = 4096, T = 8192): D = 1, N = 8 120.2 against 124.5 us;
+//    N = 2 53.3 against 54.0.
+//  * 512 x 4 class (h = 16384): at N = 8 every sequenced variant spills or
+//    loses occupancy (131-173 us against 124.6), so it keeps the table entry.
+// Otherwise, up to kMaxCappedPartials the table entry applies with its
+// occupancy cap; above it the cap is dropped (it would force spills).
 constexpr Geometry fused_geometry(int g, int n) {
-  if (n <= kMaxCappedPartials) return kGeometry[g];
-  if (kGeometry[g].block == 512 && kGeometry[g].vpt == 2) return Geometry{1024, 1, 1, 1};
-  return Geometry{kGeometry[g].block, kGeometry[g].vpt, 1, kGeometry[g].chunk};
+  const Geometry k = kGeometry[g];
+  if (k.block == 512 && k.vpt == 2 && n >= 5) return Geometry{1024, 1, 8, 1, n >= 7 ? 1 : 2};
+  if (k.block == 512 && k.vpt == 1 && n >= 2) return Geometry{512, 1, 8, 1, 1};
+  if (n <= kMaxCappedPartials) return k;
+  return Geometry{k.block, k.vpt, 1, k.chunk, k.seq};
 }
+// The sequenced load order wins only once a launch fills every CU with
+// resident workgroups: with fewer rows each workgroup waits out its tensors
+// one latency at a time, and issuing all loads at once is faster (T = 128,
+// N = 8, h = 8192: 7.05 us against 9.34; h = 4096 at T = 512: 9.99 against
+// 11.05).  The crossover is one full round of workgroups: 256 CUs times the
+// workgroups that fit on a CU at 8 waves per SIMD (512 rows for 1024 x 1,
+// 1024 for 512 x 1).  Both orders do the same arithmetic, so the choice
+// never changes a bit of the result.
+constexpr int kNumCUs = 256;
+constexpr int64_t seq_min_workgroups(int block) { return (int64_t)kNumCUs * (8 * 4 * 64 / block); }
+
 constexpr int kNumGeometries = sizeof(kGeometry) / sizeof(kGeometry[0]);
 constexpr int kMaxVectors = 8192;
 

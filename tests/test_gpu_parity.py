@@ -510,3 +510,29 @@ def test_row_whose_sum_of_squares_overflows_float32():
     y, x, _ = _oracle(d, rows=[0, 2])
     check(out[[0, 2]], y, "bf16", "out, other rows")
     check(rout[[0, 2]], x, "bf16", "residual_out, other rows")
+
+
+@pytest.mark.parametrize("h,N", [(8192, 5), (8192, 6), (8192, 8), (8192, 16), (4096, 2), (4096, 8)])
+def test_load_order_never_changes_a_bit(h, N):
+    # A launch that fills every CU loads the tensors in summation order; a
+    # smaller one (here each of the N shards) issues all loads at once.  The
+    # arithmetic is the same, so every row must come out bit-identical, and
+    # both must meet the oracle.
+    T = 1100                       # above one full round at both widths (512 / 1024 rows)
+    d = make_inputs("llama70b", num_tokens=T, hidden=h, seed=40 + N)
+    # N partials: the eight drawn ones, then the same rows in reverse order.
+    d["partials"] = np.concatenate([d["partials"], d["partials"][:, ::-1]])[:N]
+    parts, res, w = upload(d)
+    say(f"load orders: T={T} h={h} N={N}")
+    out, rout = _run_full(parts, res, w, d["eps"])
+    out_s = torch.full_like(res, float("nan"))
+    rout_s = torch.full_like(res, float("nan"))
+    for k in range(N):
+        tw.tw_shard_rmsnorm(parts, res, w, d["eps"], shard_index=k, out=out_s, residual_out=rout_s)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(out_s), out)
+    np.testing.assert_array_equal(to_host(rout_s), rout)
+    rows = list(range(0, T, 37))
+    y, x, _ = _oracle(d, rows=rows)
+    check(out[rows], y, "bf16", "out")
+    check(rout[rows], x, "bf16", "residual_out")
