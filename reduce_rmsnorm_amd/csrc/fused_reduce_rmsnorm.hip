@@ -119,7 +119,7 @@ _Pragma("unroll")                                                               
   }                                                                                    \
                                                                                        \
   u32x4 wraw[VPT];                                                                     \
-  if constexpr (SEQ > 0 || CHUNK == VPT) {                                             \
+  if constexpr (CHUNK == VPT) {                                                        \
 _Pragma("unroll")                                                                      \
     for (int j = 0; j < VPT; ++j) wraw[j] = a.weight[vi[j]];                           \
   }                                                                                    \
@@ -128,39 +128,42 @@ _Pragma("unroll")                                                               
   float x[VPT][E];                                                                     \
   float ss = 0.0f;                                                                     \
   if constexpr (SEQ > 0) {                                                             \
-    u32x4 raw[N + 1][VPT];                                                             \
-    float s[VPT][E], c[VPT][E];                                                        \
 _Pragma("unroll")                                                                      \
-    for (int i = 0; i < SEQ && i <= N; ++i)                                            \
+    for (int j0 = 0; j0 < VPT; j0 += CHUNK) {                                          \
+      u32x4 raw[N + 1][CHUNK];                                                         \
+      float s[CHUNK][E], c[CHUNK][E];                                                  \
 _Pragma("unroll")                                                                      \
-      for (int j = 0; j < VPT; ++j)                                                    \
-        raw[i][j] = __builtin_nontemporal_load(TW_TENSOR(i) + base + vi[j]);           \
+      for (int i = 0; i < SEQ && i <= N; ++i)                                          \
 _Pragma("unroll")                                                                      \
-    for (int i = 0; i <= N; ++i) {                                                     \
-      __builtin_amdgcn_sched_barrier(0);                                               \
+        for (int jj = 0; jj < CHUNK; ++jj)                                             \
+          raw[i][jj] = __builtin_nontemporal_load(TW_TENSOR(i) + base + vi[j0 + jj]);  \
 _Pragma("unroll")                                                                      \
-      for (int j = 0; j < VPT; ++j) {                                                  \
-        if (i == 0) {                                                                  \
-          unpack<BF16>(raw[0][j], s[j]);                                               \
+      for (int i = 0; i <= N; ++i) {                                                   \
+        __builtin_amdgcn_sched_barrier(0);                                             \
 _Pragma("unroll")                                                                      \
-          for (int e = 0; e < E; ++e) c[j][e] = 0.0f;                                  \
-        } else {                                                                       \
-          float t[E];                                                                  \
-          unpack<BF16>(raw[i][j], t);                                                  \
+        for (int jj = 0; jj < CHUNK; ++jj) {                                           \
+          if (i == 0) {                                                                \
+            unpack<BF16>(raw[0][jj], s[jj]);                                           \
 _Pragma("unroll")                                                                      \
-          for (int e = 0; e < E; ++e) two_sum_into(s[j][e], c[j][e], t[e]);            \
+            for (int e = 0; e < E; ++e) c[jj][e] = 0.0f;                               \
+          } else {                                                                     \
+            float t[E];                                                                \
+            unpack<BF16>(raw[i][jj], t);                                               \
+_Pragma("unroll")                                                                      \
+            for (int e = 0; e < E; ++e) two_sum_into(s[jj][e], c[jj][e], t[e]);        \
+          }                                                                            \
+        }                                                                              \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+        if (i + SEQ <= N) {                                                            \
+_Pragma("unroll")                                                                      \
+          for (int jj = 0; jj < CHUNK; ++jj)                                           \
+            raw[i + SEQ <= N ? i + SEQ : N][jj] =                                      \
+                __builtin_nontemporal_load(TW_TENSOR(i + SEQ) + base + vi[j0 + jj]);   \
         }                                                                              \
       }                                                                                \
-      __builtin_amdgcn_sched_barrier(0);                                               \
-      if (i + SEQ <= N) {                                                              \
 _Pragma("unroll")                                                                      \
-        for (int j = 0; j < VPT; ++j)                                                  \
-          raw[i + SEQ <= N ? i + SEQ : N][j] =                                         \
-              __builtin_nontemporal_load(TW_TENSOR(i + SEQ) + base + vi[j]);           \
-      }                                                                                \
+      for (int jj = 0; jj < CHUNK; ++jj) TW_FINISH_SLOT(j0 + jj, s[jj], c[jj])         \
     }                                                                                  \
-_Pragma("unroll")                                                                      \
-    for (int j = 0; j < VPT; ++j) TW_FINISH_SLOT(j, s[j], c[j])                        \
   } else {                                                                             \
 _Pragma("unroll")                                                                      \
     for (int j0 = 0; j0 < VPT; j0 += CHUNK) {                                          \
@@ -191,7 +194,7 @@ _Pragma("unroll")                                                               
       if constexpr (CHUNK < VPT) __builtin_amdgcn_sched_barrier(0);                    \
     }                                                                                  \
   }                                                                                    \
-  if constexpr (SEQ == 0 && CHUNK < VPT) {                                             \
+  if constexpr (CHUNK < VPT) {                                                         \
 _Pragma("unroll")                                                                      \
     for (int j = 0; j < VPT; ++j) wraw[j] = a.weight[vi[j]];                           \
   }                                                                                    \

@@ -38,8 +38,9 @@ constexpr int kMaxCappedPartials = 8;
 // The geometry the fused kernels use for row class g and N partials.
 //
 // Loading the tensors in summation order, with only D of them in flight per
-// thread, keeps fewer DRAM regions open at once than issuing all N+1 loads
-// together, and beats it once there are enough partials.  Measured on MI355X
+// thread (over CHUNK vector slots at a time), keeps fewer DRAM regions open
+// at once than issuing all N+1 loads together, and beats it once there are
+// enough partials.  Measured on MI355X
 // (bf16, inputs and outputs rotated past the MALL):
 //  * 512 x 2 class (h = 8192): 1024 x 1 with D = 1, T = 1024: N = 7 28.3 us
 //    against 29.2; N = 8 30.8 against 31.7; N = 12 40.5 against 44.0; N = 16
@@ -48,14 +49,18 @@ constexpr int kMaxCappedPartials = 8;
 //    loading everything at once stays best (N = 2: 16.0 against 16.6 us).
 //  * 512 x 1 class (h = 4096, T = 8192): D = 1, N = 8 120.2 against 124.5 us;
 //    N = 2 53.3 against 54.0.
-//  * 512 x 4 class (h = 16384): at N = 8 every sequenced variant spills or
-//    loses occupancy (131-173 us against 124.6), so it keeps the table entry.
+//  * 512 x 4 class (h = 16384, T = 2048): 1024 x 2 loading one vector slot
+//    at a time, each in sequence with one tensor in flight (46 VGPRs, 8 waves
+//    per SIMD): N = 2 56.8 against 59.5 us, N = 4 77.8 against 79.7, N = 8
+//    120.7 against 124.6.  Sequencing all four slots of 512 x 4 at once
+//    spills or loses occupancy instead.
 // Otherwise, up to kMaxCappedPartials the table entry applies with its
 // occupancy cap; above it the cap is dropped (it would force spills).
 constexpr Geometry fused_geometry(int g, int n) {
   const Geometry k = kGeometry[g];
   if (k.block == 512 && k.vpt == 2 && n >= 5) return Geometry{1024, 1, 8, 1, n >= 7 ? 1 : 2};
   if (k.block == 512 && k.vpt == 1 && n >= 2) return Geometry{512, 1, 8, 1, 1};
+  if (k.block == 512 && k.vpt == 4 && n >= 2) return Geometry{1024, 2, 8, 1, 1};
   if (n <= kMaxCappedPartials) return k;
   return Geometry{k.block, k.vpt, 1, k.chunk, k.seq};
 }
