@@ -14,10 +14,11 @@
 //                                                                  1 read,  1 write
 //
 // so (N+3) reads and 3 writes against the fused kernel's (N+1) and 2.  The
-// arithmetic matches the fused kernel (compensated float32 sums, correctly
-// rounded stores, the same wave/LDS reduction order, the same geometry table);
-// what differs is the rounding of the intermediate tensors, which the unfused
-// flow stores and reads back.
+// arithmetic is the fused kernel's kind (compensated float32 sums, correctly
+// rounded stores, a wave/LDS sum of squares in a fixed order); what differs is
+// the rounding of the intermediate tensors, which the unfused flow stores and
+// reads back.  The reduce step streams with the fused kernel's geometry and
+// load orders; the add + RMSNorm step uses the plain row table.
 
 #include <hip/hip_runtime.h>
 
@@ -51,8 +52,13 @@ struct AddNormArgs {
   float eps;
 };
 
-template <int N, int BLOCK, int VPT, bool BF16>
-__global__ __launch_bounds__(BLOCK) void reduce_kernel(ReduceArgs a) {
+// The reduce step uses the fused kernel's row geometry and load orders (all
+// loads of CHUNK slots at once, or the partials in summation order with SEQ in
+// flight), so that the comparator streams as well as the fused kernel does.
+// No value is shared between threads, so the geometry never changes a bit.
+template <int N, int BLOCK, int VPT, bool BF16, int WPE, int CHUNK, int SEQ>
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(WPE)))
+void reduce_kernel(ReduceArgs a) {
   constexpr int E = Elem<BF16>::kPerVec;
   const int tid = threadIdx.x;
   const int64_t base = (int64_t)blockIdx.x * a.nvec;
@@ -65,30 +71,59 @@ __global__ __launch_bounds__(BLOCK) void reduce_kernel(ReduceArgs a) {
     valid[j] = v < nvec;
     vi[j] = valid[j] ? v : nvec - 1;
   }
-  u32x4 raw[N][VPT];
 #pragma unroll
-  for (int i = 0; i < N; ++i)
+  for (int j0 = 0; j0 < VPT; j0 += CHUNK) {
+    u32x4 raw[N][CHUNK];
+    float s[CHUNK][E], c[CHUNK][E];
+    if constexpr (SEQ > 0) {
 #pragma unroll
-    for (int j = 0; j < VPT; ++j)
-      raw[i][j] = __builtin_nontemporal_load(a.partials[i] + base + vi[j]);
+      for (int i = 0; i < SEQ && i < N; ++i)
 #pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    float s[E], c[E], t[E], keep[E];
-    unpack<BF16>(raw[0][j], s);
+        for (int jj = 0; jj < CHUNK; ++jj)
+          raw[i][jj] = __builtin_nontemporal_load(a.partials[i] + base + vi[j0 + jj]);
+    } else {
 #pragma unroll
-    for (int e = 0; e < E; ++e) c[e] = 0.0f;
+      for (int i = 0; i < N; ++i)
 #pragma unroll
-    for (int i = 1; i < N; ++i) {
-      unpack<BF16>(raw[i][j], t);
-#pragma unroll
-      for (int e = 0; e < E; ++e) two_sum_into(s[e], c[e], t[e]);
+        for (int jj = 0; jj < CHUNK; ++jj)
+          raw[i][jj] = __builtin_nontemporal_load(a.partials[i] + base + vi[j0 + jj]);
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float xe = s[e] + c[e];
-      keep[e] = BF16 ? round_to_odd(s[e], c[e], xe) : xe;
+    for (int i = 0; i < N; ++i) {
+      if constexpr (SEQ > 0) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int jj = 0; jj < CHUNK; ++jj) {
+        if (i == 0) {
+          unpack<BF16>(raw[0][jj], s[jj]);
+#pragma unroll
+          for (int e = 0; e < E; ++e) c[jj][e] = 0.0f;
+        } else {
+          float t[E];
+          unpack<BF16>(raw[i][jj], t);
+#pragma unroll
+          for (int e = 0; e < E; ++e) two_sum_into(s[jj][e], c[jj][e], t[e]);
+        }
+      }
+      if constexpr (SEQ > 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + SEQ < N) {
+#pragma unroll
+          for (int jj = 0; jj < CHUNK; ++jj)
+            raw[i + SEQ < N ? i + SEQ : N - 1][jj] = __builtin_nontemporal_load(
+                a.partials[i + SEQ < N ? i + SEQ : N - 1] + base + vi[j0 + jj]);
+        }
+      }
     }
-    if (valid[j]) a.reduced[base + vi[j]] = pack<BF16>(keep);
+#pragma unroll
+    for (int jj = 0; jj < CHUNK; ++jj) {
+      float keep[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float xe = s[jj][e] + c[jj][e];
+        keep[e] = BF16 ? round_to_odd(s[jj][e], c[jj][e], xe) : xe;
+      }
+      if (valid[j0 + jj]) a.reduced[base + vi[j0 + jj]] = pack<BF16>(keep);
+    }
   }
 }
 
@@ -158,22 +193,33 @@ __global__ __launch_bounds__(BLOCK) void add_rmsnorm_kernel(AddNormArgs a) {
 using ReduceFn = void (*)(ReduceArgs);
 using AddNormFn = void (*)(AddNormArgs);
 
-template <bool BF16, int G, int... Ns>
-constexpr std::array<ReduceFn, sizeof...(Ns)> reduce_row(std::integer_sequence<int, Ns...>) {
-  return {&reduce_kernel<Ns + 1, kGeometry[G].block, kGeometry[G].vpt, BF16>...};
+constexpr int reduce_order(int g, int n, bool seq_order) {
+  return seq_order ? fused_geometry(g, n).seq : 0;
 }
-template <bool BF16, int... Gs>
+// Occupancy cap of the reduce step: the fused geometry's, except above ten
+// partials, where the cap would make the compiler spill the loaded values.
+constexpr int reduce_waves(int g, int n) { return n <= 10 ? fused_geometry(g, n).waves_per_eu : 1; }
+template <bool BF16, bool SEQ_ORDER, int G, int... Ns>
+constexpr std::array<ReduceFn, sizeof...(Ns)> reduce_row(std::integer_sequence<int, Ns...>) {
+  return {&reduce_kernel<Ns + 1, fused_geometry(G, Ns + 1).block, fused_geometry(G, Ns + 1).vpt,
+                         BF16, reduce_waves(G, Ns + 1),
+                         fused_geometry(G, Ns + 1).chunk, reduce_order(G, Ns + 1, SEQ_ORDER)>...};
+}
+template <bool BF16, bool SEQ_ORDER, int... Gs>
 constexpr std::array<std::array<ReduceFn, kMaxPartials>, sizeof...(Gs)> reduce_table(
     std::integer_sequence<int, Gs...>) {
-  return {reduce_row<BF16, Gs>(std::make_integer_sequence<int, kMaxPartials>{})...};
+  return {reduce_row<BF16, SEQ_ORDER, Gs>(std::make_integer_sequence<int, kMaxPartials>{})...};
 }
 template <bool BF16, int... Gs>
 constexpr std::array<AddNormFn, sizeof...(Gs)> addnorm_table(std::integer_sequence<int, Gs...>) {
   return {&add_rmsnorm_kernel<kGeometry[Gs].block, kGeometry[Gs].vpt, BF16>...};
 }
 
-const auto kReduceF32 = reduce_table<false>(std::make_integer_sequence<int, kNumGeometries>{});
-const auto kReduceBF16 = reduce_table<true>(std::make_integer_sequence<int, kNumGeometries>{});
+using Geoms = std::make_integer_sequence<int, kNumGeometries>;
+// [bf16][sequenced order][row class][N - 1]
+const std::array<std::array<std::array<std::array<ReduceFn, kMaxPartials>, kNumGeometries>, 2>, 2>
+    kReduce = {{{reduce_table<false, false>(Geoms{}), reduce_table<false, true>(Geoms{})},
+                {reduce_table<true, false>(Geoms{}), reduce_table<true, true>(Geoms{})}}};
 const auto kAddNormF32 = addnorm_table<false>(std::make_integer_sequence<int, kNumGeometries>{});
 const auto kAddNormBF16 = addnorm_table<true>(std::make_integer_sequence<int, kNumGeometries>{});
 
@@ -200,10 +246,12 @@ int launch_reduce(const ReduceLaunch& L, char* err, size_t errlen) {
   for (int i = 0; i < L.num_partials; ++i) k.partials[i] = static_cast<const u32x4*>(L.partials[i]);
   k.reduced = static_cast<u32x4*>(L.reduced);
   k.nvec = (int32_t)nvec;
-  const ReduceFn fn = bf16 ? kReduceBF16[g][L.num_partials - 1] : kReduceF32[g][L.num_partials - 1];
+  const Geometry geo = fused_geometry(g, L.num_partials);
+  const ReduceFn fn =
+      kReduce[bf16][L.num_rows >= seq_min_workgroups(geo.block)][g][L.num_partials - 1];
   // Row ranges of at most max_rows_per_dispatch rows, each its own dispatch
   // with the tensors' base pointers advanced to the range's first row.
-  const int64_t chunk = max_rows_per_dispatch(kGeometry[g].block);
+  const int64_t chunk = max_rows_per_dispatch(geo.block);
   hipError_t e = hipSuccess;
   for (int64_t r0 = 0; r0 < L.num_rows && e == hipSuccess; r0 += chunk) {
     const int64_t n = L.num_rows - r0 < chunk ? L.num_rows - r0 : chunk;
@@ -212,7 +260,7 @@ int launch_reduce(const ReduceLaunch& L, char* err, size_t errlen) {
     kc.reduced = k.reduced + r0 * nvec;
     void* args[] = {&kc};
     e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)n),
-                        dim3(kGeometry[g].block), args, 0, static_cast<hipStream_t>(L.stream));
+                        dim3(geo.block), args, 0, static_cast<hipStream_t>(L.stream));
   }
   if (e != hipSuccess) {
     std::snprintf(err, errlen, "hipLaunchKernel: %s", hipGetErrorString(e));
