@@ -88,6 +88,62 @@ int main(void) {
     fail |= report("plan_zero_tile", tw_split_plan(&p, &r));
   }
   {
+    /* Randomized argument sets, each invalid by construction (an output
+     * starting exactly at another tensor, a misaligned pointer, or a bad
+     * scalar), so that argument validation must refuse every call.  As a
+     * second guard the pointer checks are on for the loop: a call that got
+     * past validation would be refused as unknown memory, never launched.
+     * The fake addresses are never dereferenced.  Exercises the validation
+     * code under the sanitizers this program may be built with. */
+    unsigned long long st = 88172645463325252ULL;
+    int it, refused = 0;
+    tw_set_pointer_checks(1);
+    for (it = 0; it < 2000; ++it) {
+      const void* parts[16];
+      unsigned long long base = 0x7f0000000000ULL, r;
+      long long T, h;
+      int n, i, kind, victim;
+      size_t row;
+      const unsigned char* p[5];
+      tw_status s;
+#define NEXT() (st ^= st << 13, st ^= st >> 7, st ^= st << 17, st)
+      r = NEXT();
+      n = 1 + (int)(r % 16);
+      T = 1 + (long long)((r >> 8) % 64);
+      h = 8 * (1 + (long long)((r >> 16) % 32));
+      row = (size_t)(T * h * 2);
+      for (i = 0; i < n; ++i) parts[i] = (const void*)(base + (unsigned long long)i * (row + 4096));
+      for (i = 0; i < 4; ++i) p[i] = (const unsigned char*)(base + (unsigned long long)(n + i) * (row + 4096));
+      p[4] = p[0];
+      kind = (int)((r >> 24) % 4);
+      victim = (int)((r >> 32) % (unsigned long long)(n + 2));
+      if (kind == 0) {          /* out starts at an input */
+        p[2] = victim < n ? (const unsigned char*)parts[victim] : p[victim - n];
+      } else if (kind == 1) {   /* residual_out starts at a partial or the weight */
+        p[3] = victim < n ? (const unsigned char*)parts[victim] : p[1];
+      } else if (kind == 2) {   /* misaligned output */
+        p[2] = p[2] + 8;
+      } else {                  /* a bad scalar */
+        h = (r >> 40) % 2 ? h + 1 : h;
+        if (h % 8 == 0) T = -T;
+      }
+      s = tw_fused_reduce_rmsnorm(parts, n, p[0], p[1], (void*)p[2], (void*)p[3], T, h, 1e-5f,
+                                  TW_BF16, NULL);
+      if (s != TW_OK && tw_last_error()[0] != '\0' && strstr(tw_last_error(), "memory") == NULL &&
+          strstr(tw_last_error(), "allocation") == NULL)
+        ++refused;
+      else {
+        fprintf(stderr, "case %d (kind %d) not refused by validation: status %d (%s)\n", it, kind,
+                (int)s, tw_last_error());
+        fail = 1;
+        break;
+      }
+#undef NEXT
+    }
+    tw_set_pointer_checks(0);
+    printf("randomized_refused %d\n", refused == 2000 ? 0 : 1);
+  }
+  {
     int k;
     for (k = 0; k <= 3; ++k)
       if (tw_status_string((tw_status)k) == NULL || tw_status_string((tw_status)k)[0] == '\0') {

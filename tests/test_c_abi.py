@@ -29,6 +29,7 @@ EXPECTED_STATUS = {
     "empty_batch": _lib.TW_OK,
     "plan_null_problem": _lib.TW_ERR_INVALID_ARG,
     "plan_zero_tile": _lib.TW_ERR_INVALID_ARG,
+    "randomized_refused": 0,      # 0: every randomized invalid call was refused
 }
 
 
@@ -73,5 +74,51 @@ def test_c_program_matches_oracle(tmp_path, cases, compiler, std, lang):
         want = oracle.split_plan(T, tokens_per_cta=tpc, ctas_per_token_tile=tiles, num_cus=cus,
                                  ctas_per_cu=occ, min_split_tokens=thr)
         assert got[1:] == [want[f] for f in FIELDS], (c, got, want)
+    checks = dict(ln.split() for ln in lines[len(cases):-1])
+    assert {k: int(v) for k, v in checks.items()} == EXPECTED_STATUS
+
+
+def test_c_program_under_address_and_undefined_sanitizers(tmp_path, cases):
+    """The host code (argument validation, split planner) built with
+    AddressSanitizer and UndefinedBehaviorSanitizer, driven by the same C
+    program: every planner case, every error path and 2000 randomized invalid
+    calls, with no sanitizer report.  Host code only: the kernels are linked
+    from the regular build and never launched."""
+    from reduce_rmsnorm_amd import build as B
+    objs = [os.path.join(B.BUILD, s + ".o") for s in B.HIP_SOURCES]
+    if not all(os.path.exists(o) for o in objs):
+        pytest.skip("kernel objects not built (run the build first)")
+    for tool in ("gcc", "g++"):
+        if shutil.which(tool) is None:
+            pytest.skip(f"{tool} not installed")
+    san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-g", "-O1"]
+    host = []
+    for src in B.HOST_SOURCES:
+        o = str(tmp_path / (src + ".o"))
+        subprocess.run(["g++", "-std=c++17", *san, "-fPIC", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                        "-I", os.path.join(ROOT, "include"), "-c", os.path.join(B.CSRC, src), "-o", o],
+                       check=True, capture_output=True, text=True)
+        host.append(o)
+    main_o = str(tmp_path / "abi_check.o")
+    subprocess.run(["gcc", "-std=c99", *san, "-I", os.path.join(ROOT, "include"), "-c", SRC, "-o", main_o],
+                   check=True, capture_output=True, text=True)
+    exe = str(tmp_path / "abi_check_san")
+    link = subprocess.run(["g++", *san, main_o, *host, *objs, "-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib",
+                           "-lamdhip64", "-o", exe], capture_output=True, text=True)
+    if link.returncode != 0:
+        pytest.skip(f"sanitizer link unavailable: {link.stderr[-300:]}")
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    stdin = "".join(" ".join(str(v) for v in c) + "\n" for c in cases)
+    run = subprocess.run([exe], input=stdin, capture_output=True, text=True, timeout=120, env=env)
+    assert run.returncode == 0, run.stderr[-2000:]
+    assert "runtime error" not in run.stderr and "AddressSanitizer" not in run.stderr, run.stderr[-2000:]
+    lines = run.stdout.splitlines()
+    assert lines[-1] == "done"
+    for c, ln in zip(cases, lines[:len(cases)]):
+        T, tpc, tiles, cus, occ, thr = c
+        want = oracle.split_plan(T, tokens_per_cta=tpc, ctas_per_token_tile=tiles, num_cus=cus,
+                                 ctas_per_cu=occ, min_split_tokens=thr)
+        assert [int(v) for v in ln.split()][1:] == [want[f] for f in FIELDS], (c, ln)
     checks = dict(ln.split() for ln in lines[len(cases):-1])
     assert {k: int(v) for k, v in checks.items()} == EXPECTED_STATUS
