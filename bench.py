@@ -74,6 +74,11 @@ def parse():
                     help="also time one tensor-parallel layer step (row-parallel GEMM + fused "
                          "step) unsplit and split in two on two streams, for every offset, at "
                          "several token counts: the measured offset sweep")
+    ap.add_argument("--overlap-tokens", default="1024,2048,4096,8192",
+                    help="token counts of the --overlap sweep (comma separated)")
+    ap.add_argument("--overlap-lean", action="store_true",
+                    help="--overlap: time only the unsplit step and the split offsets (no "
+                         "confined-workgroup or per-component runs), for long token lists")
     ap.add_argument("--split-table", action="store_true",
                     help="also time the fused step alone as two launches (prefix, suffix) for "
                          "every offset, next to one launch over all rows")
@@ -216,16 +221,18 @@ def _on(stream, fn, i):
         fn(i)
 
 
-def run_overlap(tw, torch, wl, plan_kw) -> list:
+def run_overlap(tw, torch, wl, plan_kw, token_counts, lean=False) -> dict:
     """For each token count: the unsplit step and every feasible split offset,
     each captured as a HIP graph per rotated buffer set and replayed (no host
-    launch cost), plus the eager (Python-launched) times for reference."""
+    launch cost), plus the eager (Python-launched) times for reference.  Also
+    the pages' offline table: per token count, the fastest of unsplit and the
+    split offsets, next to what the analytic planner chose."""
     from reduce_rmsnorm_amd.overlap import LayerStep, capture, time_graphs, time_steps
     # Two side streams, default priority (graphs are captured off the null stream).
     stream_a = torch.cuda.Stream()
     stream_b = torch.cuda.Stream()
     rows = []
-    for T in (1024, 2048, 4096, 8192):
+    for T in token_counts:
         nsets = rotation_sets(T, wl.hidden, wl.num_partials, 2)
         step = LayerStep(T, wl.hidden, OVERLAP_K, wl.num_partials, eps=wl.eps, sets=nsets)
         iters = max(20, int(4e-3 / (T * 4e-9 + 1e-6)))
@@ -253,6 +260,14 @@ def run_overlap(tw, torch, wl, plan_kw) -> list:
         best = min(entry["splits"], key=lambda e: e["us"])
         entry["best_offset"] = best["offset"]
         entry["best_speedup"] = best["speedup"]
+        if lean:
+            rows.append(entry)
+            print(f"[bench] overlap T={T} (graph replay): unsplit {base:.1f} us; " + ", ".join(
+                f"off {e['offset']}: {e['us']:.1f}" for e in entry["splits"]) +
+                f"; planner reason {plan['reason']} off {plan['offset']}", file=sys.stderr, flush=True)
+            del step
+            torch.cuda.empty_cache()
+            continue
         # The fused kernel confined to G workgroups during the overlap (the
         # pages run theirs on a few SMs so the GEMM keeps the rest).
         entry["splits_workgroups"] = []
@@ -284,7 +299,19 @@ def run_overlap(tw, torch, wl, plan_kw) -> list:
             f"; components {entry['components_us']}", file=sys.stderr, flush=True)
         del step
         torch.cuda.empty_cache()
-    return rows
+    table = []
+    for e in rows:
+        choices = {-1: e["unsplit_us"]}
+        choices.update({s["offset"]: s["us"] for s in e["splits"]})
+        fastest = min(choices, key=choices.get)
+        pl = e["planner"]["offset"] if e["planner"]["reason"] == 0 else -1
+        table.append({"tokens": e["tokens"], "fastest": fastest, "fastest_us": choices[fastest],
+                      "best_split_offset": e["best_offset"],
+                      "best_split_us": choices[e["best_offset"]],
+                      "planner": pl, "planner_us": choices.get(pl),
+                      "planner_over_fastest": round(choices[pl] / choices[fastest] - 1, 4)
+                      if pl in choices else None})
+    return {"steps": rows, "table": table}
 
 
 def _probe_lib():
@@ -651,7 +678,8 @@ def main():
 
     overlap = None
     if args.overlap:
-        overlap = run_overlap(tw, torch, wl, plan_kw)
+        overlap = run_overlap(tw, torch, wl, plan_kw,
+                              [int(t) for t in args.overlap_tokens.split(",")], args.overlap_lean)
 
     ceiling = None
     if args.ceiling:
