@@ -14,17 +14,20 @@ The Python names mirror the C entry points:
   reduction, then a standard two-pass residual-add + RMSNorm).
 
 :class:`PreparedFused` marshals a launch once for loops that repeat it, and
-:class:`SplitPlanCache` keeps one split plan per token count.
+:class:`SplitPlanCache` keeps one split plan per token count, optionally taken
+from a measured offline table (:func:`split_table_from_sweep`).
 """
 
 from ._lib import (  # noqa: F401
     LIB_PATH,
+    PLAN_MEASURED_UNSPLIT,
     PLAN_REASONS,
     PreparedFused,
     SplitPlanCache,
     TokenWeaveError,
     declared_functions,
     load_library,
+    split_table_from_sweep,
     tw_fused_reduce_rmsnorm,
     tw_fused_reduce_rmsnorm_grid,
     tw_add_rmsnorm,

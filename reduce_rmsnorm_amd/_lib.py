@@ -26,9 +26,14 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tokenweave.h")
 TW_OK, TW_ERR_INVALID_ARG, TW_ERR_UNSUPPORTED, TW_ERR_DEVICE = 0, 1, 2, 3
 TW_F32, TW_BF16 = 0, 1
 TW_MAX_PARTIALS = 16
+TW_PLAN_SPLIT, TW_PLAN_BELOW_THRESHOLD, TW_PLAN_SINGLE_WAVE = 0, 1, 2
+TW_PLAN_NO_FEASIBLE_OFFSET, TW_PLAN_EMPTY = 3, 4
+# Reason code of a plan taken from a measured table that keeps the batch
+# whole (the C planner's own codes are the TW_PLAN_* above).
+PLAN_MEASURED_UNSPLIT = 5
 
 PLAN_REASONS = {0: "split", 1: "below_threshold", 2: "single_wave", 3: "no_feasible_offset",
-                4: "empty"}
+                4: "empty", 5: "measured_unsplit"}
 
 
 class TokenWeaveError(RuntimeError):
@@ -344,15 +349,46 @@ class PreparedFused:
 
 class SplitPlanCache:
     """Split plans by token count for one model/GEMM configuration: each
-    count is planned once by tw_split_plan and then looked up, as the pages
-    keep the chosen split of each shape in a table."""
+    count is planned once and then looked up, as the pages keep the chosen
+    split of each shape in a table.
 
-    def __init__(self, **problem):
+    ``measured`` optionally maps token counts to the offset an offline sweep
+    found fastest (-1: keep the batch whole), the way the pages choose their
+    offsets by timing.  A count in it gets that split; any other count gets
+    tw_split_plan's analytic plan.  The wave fields always come from the
+    analytic planner."""
+
+    def __init__(self, measured: Optional[dict] = None, **problem):
         self._problem = problem
+        self._measured = {}
+        for t, off in (measured or {}).items():
+            t, off = int(t), int(off)
+            if t < 1 or not (off == -1 or 0 <= off < t // 2):
+                raise ValueError(f"measured split for {t} tokens: offset {off} outside [0, T/2) or -1")
+            self._measured[t] = off
         self._plans = {}
 
     def __call__(self, num_tokens: int) -> dict:
         plan = self._plans.get(num_tokens)
         if plan is None:
-            plan = self._plans[num_tokens] = tw_split_plan(num_tokens, **self._problem)
+            plan = tw_split_plan(num_tokens, **self._problem)
+            off = self._measured.get(num_tokens)
+            if off is not None:
+                plan = dict(plan)
+                if off < 0:
+                    plan.update(prefix_tokens=num_tokens, suffix_tokens=0, offset=-1,
+                                reason=PLAN_MEASURED_UNSPLIT)
+                else:
+                    prefix = num_tokens // 2 + off
+                    plan.update(prefix_tokens=prefix, suffix_tokens=num_tokens - prefix,
+                                offset=off, reason=TW_PLAN_SPLIT)
+            self._plans[num_tokens] = plan
         return plan
+
+
+def split_table_from_sweep(rows) -> dict:
+    """The offline table from a measured sweep: ``rows`` are records with
+    "tokens" and "fastest" (the fastest offset, or -1 for unsplit), such as
+    the "table" that ``bench.py --overlap`` reports.  Returns {tokens: offset}
+    for SplitPlanCache(measured=...)."""
+    return {int(r["tokens"]): int(r["fastest"]) for r in rows}

@@ -6,6 +6,8 @@ No call here reaches a kernel launch: each fused/shard call carries at least
 one invalid argument, or num_tokens == 0 (a documented no-op)."""
 
 import ctypes
+import os
+import re
 import random
 import subprocess
 
@@ -315,3 +317,33 @@ def test_last_error_is_per_thread(lib):
         t.join()
     assert all(b"eps" in m for m in results[0])
     assert all(b"multiple" in m for m in results[1])
+
+
+def test_plan_constants_match_the_header():
+    text = open(os.path.join(os.path.dirname(_lib.LIB_PATH), "..", "include", "tokenweave.h")).read()
+    for name in ("TW_PLAN_SPLIT", "TW_PLAN_BELOW_THRESHOLD", "TW_PLAN_SINGLE_WAVE",
+                 "TW_PLAN_NO_FEASIBLE_OFFSET", "TW_PLAN_EMPTY"):
+        m = re.search(rf"#define {name} (\d+)", text)
+        assert m and int(m.group(1)) == getattr(_lib, name), name
+        assert tw.PLAN_REASONS[getattr(_lib, name)]
+    assert tw.PLAN_MEASURED_UNSPLIT not in range(5)
+
+
+def test_split_plan_cache_with_a_measured_table():
+    problem = dict(tokens_per_cta=256, ctas_per_token_tile=32, num_cus=256, min_split_tokens=1024)
+    table = tw.split_table_from_sweep([{"tokens": 5632, "fastest": 128},
+                                       {"tokens": 4096, "fastest": -1}])
+    cache = tw.SplitPlanCache(measured=table, **problem)
+    analytic = oracle.split_plan(5632, **problem)
+    p = cache(5632)
+    assert analytic["reason"] == oracle.REASON_NO_FEASIBLE_OFFSET      # the planner would not split
+    assert (p["prefix_tokens"], p["suffix_tokens"], p["offset"], p["reason"]) == (2944, 2688, 128, 0)
+    assert p["waves_unsplit"] == analytic["waves_unsplit"]
+    q = cache(4096)
+    assert (q["prefix_tokens"], q["suffix_tokens"], q["offset"], q["reason"]) == \
+        (4096, 0, -1, tw.PLAN_MEASURED_UNSPLIT)
+    assert cache(3072) == oracle.split_plan(3072, **problem)           # not in the table: analytic
+    assert cache(5632) is cache(5632)
+    for bad in ({100: 50}, {100: -2}, {0: -1}):
+        with pytest.raises(ValueError):
+            tw.SplitPlanCache(measured=bad, **problem)
