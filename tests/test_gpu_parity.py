@@ -512,13 +512,17 @@ def test_row_whose_sum_of_squares_overflows_float32():
     check(rout[[0, 2]], x, "bf16", "residual_out, other rows")
 
 
-@pytest.mark.parametrize("h,N", [(8192, 5), (8192, 6), (8192, 8), (8192, 16), (4096, 2), (4096, 8)])
+@pytest.mark.parametrize("h,N", [(8192, 5), (8192, 6), (8192, 8), (8192, 16), (4096, 2), (4096, 8),
+                                 (8184, 8), (12296, 3), (16384, 8), (3080, 4)])
 def test_load_order_never_changes_a_bit(h, N):
     # A launch that fills every CU loads the tensors in summation order; a
     # smaller one (here each of the N shards) issues all loads at once.  The
     # arithmetic is the same, so every row must come out bit-identical, and
     # both must meet the oracle.
-    T = 1100                       # above one full round at both widths (512 / 1024 rows)
+    # Above one full round of workgroups at every width here (512 rows for the
+    # 1024-thread classes, 1024 rows for 512 x 1); the ragged widths (8184,
+    # 12296, 3080) leave lanes that clamp their address inside the sequence.
+    T = 1100
     d = make_inputs("llama70b", num_tokens=T, hidden=h, seed=40 + N)
     # N partials: the eight drawn ones, then the same rows in reverse order.
     d["partials"] = np.concatenate([d["partials"], d["partials"][:, ::-1]])[:N]
