@@ -743,6 +743,9 @@ def main():
     if staircase is not None:
         result["gemm_staircase"] = staircase
     if ceiling is not None:
+        # Secondary context: the fused step against a plain stream that moves
+        # exactly its bytes on the same buffers in the same run.
+        ceiling["fused_over_read_write_probe"] = round(result["value"] / ceiling["read_write_gbs"], 4)
         result["ceiling"] = ceiling
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -46,15 +46,33 @@ def _source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def _medians(trace_path: str) -> dict:
+    """Median dispatch duration (ns) per kernel name from a kernel_trace.csv."""
+    durs = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_path)):
+        durs[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = {}
+    for name, v in durs.items():
+        v.sort()
+        n = len(v)
+        out[name] = v[n // 2] if n % 2 else (v[n // 2 - 1] + v[n // 2]) / 2
+    return out
+
+
 def stats(path: str, command: str, out: str) -> None:
     rows = list(csv.DictReader(open(path)))
+    # The per-dispatch trace of the same run, when present, gives the median.
+    trace = path.replace("kernel_stats.csv", "kernel_trace.csv")
+    med = _medians(trace) if trace != path and os.path.exists(trace) else {}
     lines = [f"# rocprofv3 kernel statistics: {os.path.basename(out)[:-3]}", "",
              "Command (run from /tmp with TMPDIR=/tmp, repo at $R):", "", "```", command, "```", "",
-             "| Kernel | Calls | Avg us | Min us | Max us | StdDev us | % time |",
-             "|---|---|---|---|---|---|---|"]
+             "| Kernel | Calls | Avg us | Median us | Min us | Max us | StdDev us | % time |",
+             "|---|---|---|---|---|---|---|---|"]
     for r in rows:
-        lines.append("| `{}` | {} | {:.3f} | {:.3f} | {:.3f} | {:.3f} | {:.2f} |".format(
-            r["Name"], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+        m = med.get(r["Name"])
+        lines.append("| `{}` | {} | {:.3f} | {} | {:.3f} | {:.3f} | {:.3f} | {:.2f} |".format(
+            r["Name"], r["Calls"], float(r["AverageNs"]) / 1e3,
+            "-" if m is None else f"{m / 1e3:.3f}", float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["StdDev"]) / 1e3, float(r["Percentage"])))
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
