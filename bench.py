@@ -24,7 +24,6 @@ float64 CPU oracle on a bounded sample of the same workload on one host core.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -38,7 +37,6 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, decimal GB/s
 MALL_BYTES = 256 * 1000 * 1000  # MI355X Infinity Cache (last-level, memory side)
 MAX_ROTATE = 2048
-KERNEL_SOURCE = os.path.join(ROOT, "reduce_rmsnorm_amd", "csrc", "fused_reduce_rmsnorm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_reduce_rmsnorm_llama70b_traffic.json")
 METRIC = "fused reduce-add-RMSNorm HBM GB/s (% of peak), h=8192 T=1024 N=8 bf16"
 
@@ -47,8 +45,8 @@ GEMM_TILE = 256
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    from reduce_rmsnorm_amd.rocprof_summary import kernel_code_hash
+    return kernel_code_hash()
 
 
 def parse():
@@ -701,7 +699,7 @@ def main():
     if os.path.exists(TRAFFIC_FILE) and args.mode == "full" and wl.name == "llama70b":
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("kernel_source_sha256") == kernel_source_hash():
+        if tr.get("kernel_code_sha256") == kernel_source_hash():
             traffic = tr.get("bytes_per_launch")
 
     result = {

@@ -18,13 +18,16 @@
 //  * One workgroup per token row.  Each thread owns VPT 16-byte vectors of the
 //    row (vector v = tid + j*BLOCK), so every load and store instruction of a
 //    wave covers 1 KiB of contiguous memory.
-//  * With few partials all (N+1)*VPT loads of a thread are issued before
-//    the first use (wide rows issue them a few vector slots at a time).  With
-//    five or more partials on rows of 512-1024 vectors the tensors are loaded
-//    in summation order with one or two in flight per thread: fewer DRAM
-//    regions are open across the chip at a time, and the stream is faster.
-//    Out of range vectors (h not a multiple of BLOCK*VPT*elems) load a
-//    clamped, valid address and contribute zero, so no branch splits a load
+//  * Two load orders with the same arithmetic.  Either all (N+1)*VPT loads
+//    of a thread are issued before the first use (wide rows issue them a few
+//    vector slots at a time), or the tensors are loaded in summation order
+//    with one or two in flight per thread, so that fewer DRAM regions are
+//    open across the chip at a time and the stream is faster.  The geometry
+//    table (geometry.h) says which row classes and partial counts use the
+//    sequenced order; a launch too small to fill the CUs issues all loads at
+//    once regardless, since it would otherwise wait out one latency per
+//    tensor.  Out of range vectors (h not a multiple of BLOCK*VPT*elems) load
+//    a clamped, valid address and contribute zero, so no branch splits a load
 //    batch.
 //  * The partials and the residual are summed with an error-free
 //    transformation (TwoSum) into a float32 pair (s, c); x = s + c.  For bf16
@@ -34,8 +37,9 @@
 //  * The sum of squares is reduced within a wave64 with DPP (quad_perm,
 //    row_half_mirror, row_mirror), ds_swizzle (swap 16) and two readlanes,
 //    then across waves through LDS in wave order.  The order depends only on
-//    the kernel geometry, which depends only on h and the element size, so a
-//    row gives the same bits whichever launch (full, shard, split) runs it.
+//    the kernel geometry, which depends only on h, the element size and N (not
+//    on the launch or its load order), so a row gives the same bits whichever
+//    launch (full, shard, split, grid) runs it.
 //  * Partials and residual are streamed with non-temporal loads, the outputs
 //    with non-temporal stores; the weight row (read by every workgroup) uses
 //    ordinary loads so it stays in L2.

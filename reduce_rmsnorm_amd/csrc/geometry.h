@@ -1,5 +1,6 @@
 // Row geometry of the row-per-workgroup kernels: threads per workgroup and
-// 16-byte vectors per thread, chosen from the row width alone.  Every kernel
+// 16-byte vectors per thread, chosen from the row width (and, through
+// fused_geometry, the partial count) alone.  Every kernel
 // that normalizes rows uses this table, so the per-row arithmetic (and its
 // reduction order) never depends on the launch.
 #pragma once

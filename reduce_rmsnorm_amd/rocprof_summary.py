@@ -32,18 +32,33 @@ import csv
 import hashlib
 import json
 import os
+import re
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SOURCE = os.path.join(ROOT, "reduce_rmsnorm_amd", "csrc", "fused_reduce_rmsnorm.hip")
+CSRC = os.path.join(ROOT, "reduce_rmsnorm_amd", "csrc")
+# The fused kernel's code: its source and the headers it is built from.
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in
+                  ("fused_reduce_rmsnorm.hip", "geometry.h", "device_common.h", "launch.h")]
 FUSED = "fused_reduce_rmsnorm_kernel"
 PROBE_READ = "probe_read<"
 PROBE_WRITE = "probe_write("
 
 
-def _source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def kernel_code_hash(paths=None) -> str:
+    """SHA-256 of the fused kernel's code with comments and whitespace
+    removed: counters taken on one version stay attached to it through
+    comment edits, and any change to the code itself (kernel, geometry table,
+    device helpers) gives a new hash.  (The sources hold no string literal
+    containing comment markers.)"""
+    h = hashlib.sha256()
+    for path in paths or KERNEL_SOURCES:
+        text = open(path, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(os.path.basename(path).encode())
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
 
 
 def _medians(trace_path: str) -> dict:
@@ -111,7 +126,7 @@ def traffic(fetch: str, write: str, workload: str, cmd_fetch: str, cmd_write: st
     write_b = fused_write * 1024 * f_write
     alg = wl.algorithmic_bytes()
     res = {
-        "kernel_source_sha256": _source_hash(),
+        "kernel_code_sha256": kernel_code_hash(),
         "workload": f"{wl.name}: T={wl.num_tokens} h={wl.hidden} N={wl.num_partials} {wl.dtype}",
         "fetch_size_kib_per_launch": round(fused_fetch, 2),
         "write_size_kib_per_launch": round(fused_write, 2),
@@ -148,7 +163,7 @@ def traffic(fetch: str, write: str, workload: str, cmd_fetch: str, cmd_write: st
           f"Traffic / algorithmic bytes = {res['traffic_over_algorithmic']:.5f} "
           "(the weight row, 16 KiB, is fetched by each XCD's L2 and is not in the "
           "algorithmic count).", "",
-          f"Kernel source sha256: `{res['kernel_source_sha256']}`"]
+          f"Kernel code sha256 (comments and whitespace removed; kernel source and headers): `{res['kernel_code_sha256']}`"]
     with open(out + ".md", "w") as f:
         f.write("\n".join(md) + "\n")
     print(json.dumps(res, indent=1))
