@@ -512,9 +512,13 @@ def test_row_whose_sum_of_squares_overflows_float32():
     check(rout[[0, 2]], x, "bf16", "residual_out, other rows")
 
 
-@pytest.mark.parametrize("h,N", [(8192, 5), (8192, 6), (8192, 8), (8192, 16), (4096, 2), (4096, 8),
-                                 (8184, 8), (12296, 3), (16384, 8), (3080, 4)])
-def test_load_order_never_changes_a_bit(h, N):
+@pytest.mark.parametrize("h,N,dtype", [(8192, 5, "bf16"), (8192, 6, "bf16"), (8192, 8, "bf16"),
+                                       (8192, 16, "bf16"), (4096, 2, "bf16"), (4096, 8, "bf16"),
+                                       (8184, 8, "bf16"), (12296, 3, "bf16"), (16384, 8, "bf16"),
+                                       (3080, 4, "bf16"),
+                                       (4096, 8, "f32"), (2048, 3, "f32"), (8192, 2, "f32"),
+                                       (4092, 7, "f32")])
+def test_load_order_never_changes_a_bit(h, N, dtype):
     # A launch that fills every CU loads the tensors in summation order; a
     # smaller one (here each of the N shards) issues all loads at once.  The
     # arithmetic is the same, so every row must come out bit-identical, and
@@ -523,11 +527,11 @@ def test_load_order_never_changes_a_bit(h, N):
     # 1024-thread classes, 1024 rows for 512 x 1); the ragged widths (8184,
     # 12296, 3080) leave lanes that clamp their address inside the sequence.
     T = 1100
-    d = make_inputs("llama70b", num_tokens=T, hidden=h, seed=40 + N)
-    # N partials: the eight drawn ones, then the same rows in reverse order.
-    d["partials"] = np.concatenate([d["partials"], d["partials"][:, ::-1]])[:N]
+    d = make_inputs("llama70b" if dtype == "bf16" else "tiny", num_tokens=T, hidden=h, seed=40 + N)
+    # N partials: the drawn ones, then copies with their rows in reverse order.
+    d["partials"] = np.concatenate([d["partials"]] + [d["partials"][:, ::-1]] * 8)[:N]
     parts, res, w = upload(d)
-    say(f"load orders: T={T} h={h} N={N}")
+    say(f"load orders: T={T} h={h} N={N} {dtype}")
     out, rout = _run_full(parts, res, w, d["eps"])
     out_s = torch.full_like(res, float("nan"))
     rout_s = torch.full_like(res, float("nan"))
@@ -538,5 +542,5 @@ def test_load_order_never_changes_a_bit(h, N):
     np.testing.assert_array_equal(to_host(rout_s), rout)
     rows = list(range(0, T, 37))
     y, x, _ = _oracle(d, rows=rows)
-    check(out[rows], y, "bf16", "out")
-    check(rout[rows], x, "bf16", "residual_out")
+    check(out[rows], y, dtype, "out")
+    check(rout[rows], x, dtype, "residual_out")
