@@ -88,6 +88,11 @@ void tw_set_pointer_checks(int32_t enabled);
  * NaN and infinite inputs propagate to their row.  A row whose sum of
  * squares overflows float32 (|x| above about 1.8e19) gets rs = 0 and out = 0
  * (NaN where x is infinite); residual_out is still x rounded.
+ * The order of the sum of squares depends only on hidden, dtype and N, so a
+ * row's results are bit-identical whichever entry point or batch size
+ * computes it (how a launch schedules its loads changes no bit).  The same
+ * inputs in another order of the partials may differ in the last bit of out,
+ * except where the sums are exact.
  *
  * Arguments
  *   partials      host array of num_partials device pointers, each to a
