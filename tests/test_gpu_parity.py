@@ -544,3 +544,30 @@ def test_load_order_never_changes_a_bit(h, N, dtype):
     y, x, _ = _oracle(d, rows=rows)
     check(out[rows], y, dtype, "out")
     check(rout[rows], x, dtype, "residual_out")
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-12, 1e-5, 1.0])
+def test_subnormal_tiny_and_huge_rows_with_extreme_eps(eps):
+    # Row 0: subnormal bf16 inputs (float32 subnormals once widened), where
+    # float32 squares underflow to zero; row 1: tiny normal values (~1e-30,
+    # squares underflow); row 2: large values (~1e17, squares near the top of
+    # float32); row 3: ordinary values.  eps = 0 is left out for rows whose
+    # sum of squares underflows to zero in float32 (0/0 is the documented NaN).
+    rng = np.random.default_rng(77)
+    d = make_inputs("llama70b", num_tokens=4, hidden=512, seed=77)
+    sign = lambda shape: (rng.integers(0, 2, shape).astype(np.uint16) << 15)
+    d["partials"][:, 0, :] = sign((8, 512)) | rng.integers(1, 0x80, (8, 512)).astype(np.uint16)
+    d["residual"][0, :] = sign(512) | rng.integers(1, 0x80, 512).astype(np.uint16)
+    tiny = oracle.round_f64_to_bf16_bits(rng.normal(0, 1e-30, (8, 512)))
+    d["partials"][:, 1, :] = tiny
+    d["residual"][1, :] = oracle.round_f64_to_bf16_bits(rng.normal(0, 1e-30, 512))
+    d["partials"][:, 2, :] = oracle.round_f64_to_bf16_bits(rng.normal(0, 1e17, (8, 512)))
+    d["residual"][2, :] = oracle.round_f64_to_bf16_bits(rng.normal(0, 1e17, 512))
+    parts, res, w = upload(d)
+    say(f"subnormal / tiny / huge rows, eps={eps}")
+    out, rout = _run_full(parts, res, w, eps)
+    rows = [0, 1, 2, 3] if eps > 0 else [2, 3]
+    d["eps"] = eps
+    y, x, _ = _oracle(d, rows=rows)
+    check(rout[rows], x, "bf16", "residual_out")
+    check(out[rows], y, "bf16", "out")
