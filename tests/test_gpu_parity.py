@@ -571,3 +571,22 @@ def test_subnormal_tiny_and_huge_rows_with_extreme_eps(eps):
     y, x, _ = _oracle(d, rows=rows)
     check(rout[rows], x, "bf16", "residual_out")
     check(out[rows], y, "bf16", "out")
+
+
+@pytest.mark.parametrize("N,T,h", [(12, 600, 8192), (16, 1100, 4096), (16, 520, 16384), (3, 40, 8192)])
+def test_unfused_comparator_many_partials(N, T, h):
+    # The comparator's reduce step uses the fused geometry and load orders
+    # (sequenced above one full round of workgroups), with no occupancy cap
+    # above ten partials.
+    d = make_inputs("llama70b", num_tokens=T, hidden=h, seed=60 + N)
+    d["partials"] = np.concatenate([d["partials"], d["partials"][:, ::-1]])[:N]
+    parts, res, w = upload(d)
+    say(f"unfused comparator N={N} T={T} h={h}")
+    out, rout, red = tw.tw_unfused_reduce_rmsnorm(parts, res, w, d["eps"])
+    torch.cuda.synchronize()
+    rows = list(range(0, T, 29))
+    y, x, red_ref = oracle.unfused_reduce_rmsnorm([p[rows] for p in d["partials"]], d["residual"][rows],
+                                                  d["weight"], d["eps"], "bf16")
+    check(to_host(red)[rows], oracle.bf16_bits_to_f64(red_ref), "bf16", "reduced")
+    check(to_host(rout)[rows], x, "bf16", "residual_out")
+    check(to_host(out)[rows], y, "bf16", "out")
