@@ -349,13 +349,23 @@ def placement(lib, torch, stream, records):
     return dict(sorted(cus.items()))
 
 
+def dealt_share(torch, records) -> float:
+    """After ``placement``: the share of workgroups b that ran on XCC b mod 8,
+    i.e. how far the dispatcher deals a grid's workgroups over the XCDs in
+    turn."""
+    import numpy as np
+    r = records.cpu().numpy().view(np.uint32).reshape(PLACEMENT_GRID, 4)
+    return float(((r[:, 1] & 0xF) == (r[:, 2] % 8)).mean())
+
+
 def run_cu_mask(tw, torch, wl, sets, R, w, step_bytes) -> dict:
     """CU-masked streams (``hipExtStreamCreateWithCUMask``).
 
     The runtime accepts a mask only if it leaves at least one CU on each of the
     eight XCDs (a dispatch's workgroups are dealt out over all of them), and
     mask bit b belongs to XCD b mod 8; the placement probe confirms both here by
-    counting the CUs each XCD used.  Then: (1) fused-kernel GB/s on the first k
+    counting the CUs each XCD used, and records how often workgroup b ran on XCD
+    b mod 8 on the unconfined stream.  Then: (1) fused-kernel GB/s on the first k
     mask bits, which spreads k CUs evenly over the XCDs; (2) a skewed mask, one
     XCD whole and one CU on each other XCD, against a balanced mask of about
     the same size; (3) the split layer step with the fused kernel confined to k
@@ -377,6 +387,11 @@ def run_cu_mask(tw, torch, wl, sets, R, w, step_bytes) -> dict:
         with MaskedStream(bits) as ms:
             per_xcc = placement(lib, torch, ms.stream, records)
         out["placement"][name] = per_xcc
+        if name == "all 256 bits":
+            out["dealt_b_mod_8"] = dealt_share(torch, records)
+            print(f"[bench] cu-mask placement: workgroup b ran on XCC b mod 8 for "
+                  f"{100 * out['dealt_b_mod_8']:.2f}% of {PLACEMENT_GRID} workgroups",
+                  file=sys.stderr, flush=True)
         print(f"[bench] cu-mask placement {name}: CUs used per XCD {per_xcc}",
               file=sys.stderr, flush=True)
 
