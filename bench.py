@@ -9,11 +9,14 @@ T=1024 tokens, h=8192, N=8 bf16 partials) the planner keeps the batch whole
 
 Timing: W untimed warm-up steps, then K timed steps back to back on the
 current torch stream -- the stream the library enqueues on -- between two HIP
-events, with torch.cuda.synchronize() on both sides.  Whole buffer sets
-(inputs and outputs) rotate so that the inputs, and the outputs on their own,
-touched between two uses of one set each exceed twice the 256 MB last-level
-(MALL) cache: reads are served by HBM, and no output buffer stays resident in
-that cache to absorb its writes.
+events, with torch.cuda.synchronize() on both sides.  By default W is as many
+steps as take about 100 ms: from a pause the GPU needs about 30 ms of load to
+reach its steady speed.  The host launches every step; with --graph the same
+launches are recorded into HIP graphs and the timed steps are graph replays.
+Whole buffer sets (inputs and outputs) rotate so that the inputs, and the
+outputs on their own, touched between two uses of one set each exceed twice
+the 256 MB last-level (MALL) cache: reads are served by HBM, and no output
+buffer stays resident in that cache to absorb its writes.
 
 Printed: one JSON line.  `value` is algorithmic GB/s, (N+1 reads + 2 writes)
 x T x h x sizeof(bf16) per step over the measured time per step; `roofline`
@@ -40,6 +43,14 @@ MAX_ROTATE = 2048
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_reduce_rmsnorm_llama70b_traffic.json")
 METRIC = "fused reduce-add-RMSNorm HBM GB/s (% of peak), h=8192 T=1024 N=8 bf16"
 
+# From a pause, the GPU needs about 30 ms of sustained load before launches
+# reach their steady time (its power management ramps up the clocks): the first
+# ~1000 fused launches of the 1024-row workload take 31-33 us each, the rest
+# 30.8 us (bench.py --ramp).  The default warm-up runs about three times that.
+WARMUP_SECONDS = 0.1
+RAMP_BLOCKS, RAMP_BLOCK = 60, 100
+EMPTY_LAUNCHES = 200
+
 # GEMM tile model for the split planner: 256x256 output tiles, one CTA per CU.
 GEMM_TILE = 256
 
@@ -53,13 +64,23 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: enough for about %.0f ms of work, so "
+                         "the GPU has settled under load before the timed steps)"
+                         % (1e3 * WARMUP_SECONDS))
+    ap.add_argument("--ramp", action="store_true",
+                    help="also time the first %d steps after a short pause, in blocks of %d: "
+                         "the ramp that the warm-up covers" % (RAMP_BLOCKS * RAMP_BLOCK,
+                                                                     RAMP_BLOCK))
     ap.add_argument("--workload", default="llama70b")
     ap.add_argument("--mode", choices=("full", "shard"), default="full",
                     help="full: every row; shard: shard 0's rows (one rank's share)")
     ap.add_argument("--rotate", type=int, default=0,
                     help="buffer sets to rotate through (0: enough that the inputs, and the "
                          "outputs on their own, each exceed 2x the MALL; at most 2048)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as replays of HIP graphs that hold the same launches "
+                         "(default: every step launched from the host)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget of the CPU oracle sample (0 disables the cpu_baseline leg)")
     ap.add_argument("--no-unfused", dest="unfused", action="store_false",
@@ -95,6 +116,33 @@ def parse():
     return ap.parse_args()
 
 
+def run_ramp(torch, step, stream) -> dict:
+    """Launch time from a pause: after 0.5 s idle and 20 launches, time
+    RAMP_BLOCKS blocks of RAMP_BLOCK steps back to back, one HIP event pair
+    per block."""
+    for i in range(20):
+        step(i)
+    torch.cuda.synchronize()
+    time.sleep(0.5)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(RAMP_BLOCKS + 1)]
+    ev[0].record(stream)
+    for b in range(RAMP_BLOCKS):
+        for i in range(RAMP_BLOCK):
+            step(b * RAMP_BLOCK + i)
+        ev[b + 1].record(stream)
+    torch.cuda.synchronize()
+    us = [round(ev[b].elapsed_time(ev[b + 1]) * 1e3 / RAMP_BLOCK, 3) for b in range(RAMP_BLOCKS)]
+    steady = statistics.median(us[RAMP_BLOCKS // 2:])
+    settled = next((b for b in range(RAMP_BLOCKS) if all(x <= 1.01 * steady for x in us[b:])),
+                   RAMP_BLOCKS)
+    ms_to_settle = sum(us[:settled]) * RAMP_BLOCK / 1e3
+    print(f"[bench] ramp: first block {us[0]:.2f} us/step, steady {steady:.2f}; within 1% of "
+          f"steady after {settled * RAMP_BLOCK} steps ({ms_to_settle:.1f} ms)",
+          file=sys.stderr, flush=True)
+    return {"block_steps": RAMP_BLOCK, "us_per_step": us, "steady_us": round(steady, 3),
+            "steps_to_settle": settled * RAMP_BLOCK, "ms_to_settle": round(ms_to_settle, 2)}
+
+
 def run_ceiling(sets, R, rows, h, itemsize, stream, steps, timer):
     """Time the measurement-only probes of libtw_bwprobe.so over the bench's
     own rotated buffers: sources are the partial rows and the residual rows,
@@ -124,6 +172,28 @@ def run_ceiling(sets, R, rows, h, itemsize, stream, steps, timer):
         res[key + "_gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
         print(f"[bench] probe {key}: {nbytes} B in {us:.2f} us = {res[key + '_gbs']} GB/s",
               file=sys.stderr, flush=True)
+
+    # The fixed cost of one dependent launch: an empty kernel of G workgroups
+    # of 1024 threads, EMPTY_LAUNCHES of them recorded in a HIP graph and
+    # replayed (eager launches this short would time the host instead).
+    import torch
+    cap = torch.cuda.Stream()
+    none = (ctypes.c_void_p * 1)()
+    res["empty_launch_us"] = {}
+    for grid in (1, 256, 1024, 4096):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for _ in range(EMPTY_LAUNCHES):
+                rc = lib.tw_probe_launch(4, none, 0, none, 0, 1, grid, cap.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"empty probe launch failed: {rc}")
+        for _ in range(100):            # capture idled the GPU: settle it again first
+            g.replay()
+        us = timer(lambda i, g=g: g.replay(), 20) / EMPTY_LAUNCHES
+        res["empty_launch_us"][str(grid)] = round(us, 3)
+        print(f"[bench] empty kernel, {grid} workgroups of 1024 threads: {us:.2f} us per launch "
+              f"(graph replay)", file=sys.stderr, flush=True)
+        del g
     return res
 
 
@@ -549,18 +619,22 @@ def main():
     # prepared once per rotated buffer set so the host costs one C call each.
     planner = tw.SplitPlanCache(**plan_kw)
     plan0 = planner(T)
-    launches_per_set = []
-    for parts, res, out, rout in sets:
-        if args.mode == "shard":
-            launches_per_set.append([tw.PreparedFused(parts, res, w, wl.eps, out, rout, stream,
-                                                      mode="shard", shard_index=0)])
-        elif plan0["reason"] == 0:
-            P = plan0["prefix_tokens"]
-            launches_per_set.append([
-                tw.PreparedFused([p[lo:hi] for p in parts], res[lo:hi], w, wl.eps, out[lo:hi],
-                                 rout[lo:hi], stream) for lo, hi in ((0, P), (P, T))])
-        else:
-            launches_per_set.append([tw.PreparedFused(parts, res, w, wl.eps, out, rout, stream)])
+    def prepare(st):
+        per_set = []
+        for parts, res, out, rout in sets:
+            if args.mode == "shard":
+                per_set.append([tw.PreparedFused(parts, res, w, wl.eps, out, rout, st,
+                                                 mode="shard", shard_index=0)])
+            elif plan0["reason"] == 0:
+                P = plan0["prefix_tokens"]
+                per_set.append([
+                    tw.PreparedFused([p[lo:hi] for p in parts], res[lo:hi], w, wl.eps,
+                                     out[lo:hi], rout[lo:hi], st) for lo, hi in ((0, P), (P, T))])
+            else:
+                per_set.append([tw.PreparedFused(parts, res, w, wl.eps, out, rout, st)])
+        return per_set
+
+    launches_per_set = prepare(stream)
 
     def step(i):
         plan = planner(T) if args.mode == "full" else None
@@ -569,8 +643,43 @@ def main():
             launch()
         return len(launches_per_set[i % R])
 
+    graphs = None
+    if args.graph:
+        # The same launches recorded into HIP graphs: one graph holds a whole
+        # rotation cycle (R steps), a second one the steps % R left over, so
+        # the replays run exactly the requested number of steps.  The split
+        # plan is the one fixed per shape above.  Recorded before the warm-up:
+        # capture idles the GPU (torch collects garbage first), and the timed
+        # replays must start from a GPU that has settled under load.
+        cap = torch.cuda.Stream(dev)
+        cap_sets = prepare(cap)
+
+        def record(count):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(count):
+                    for launch in cap_sets[i % R]:
+                        launch()
+            return g
+
+        full = record(R)
+        rest = record(args.steps % R) if args.steps % R else None
+        graphs = [full] * (args.steps // R) + ([rest] if rest is not None else [])
+        with torch.cuda.stream(stream):
+            full.replay()
+        torch.cuda.synchronize()
+
+    ramp = None
+    if args.ramp:
+        ramp = run_ramp(torch, step, stream)
+    if args.warmup is None:
+        # Estimated step time: the bytes at 6 TB/s plus 3 us per launch.
+        est = step_bytes / 6.0e12 + 3e-6 * len(launches_per_set[0])
+        args.warmup = max(50, math.ceil(WARMUP_SECONDS / est))
+
     print(f"[bench] workload={wl.name} mode={args.mode} rows={rows} h={h} N={N} {wl.dtype} "
-          f"rotate={R} warmup={args.warmup} steps={args.steps}", file=sys.stderr, flush=True)
+          f"rotate={R} warmup={args.warmup} steps={args.steps} "
+          f"{'graph' if args.graph else 'eager'}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -579,8 +688,14 @@ def main():
     end = torch.cuda.Event(enable_timing=True)
     launches = 0
     start.record(stream)
-    for i in range(args.steps):
-        launches += step(i)
+    if graphs is None:
+        for i in range(args.steps):
+            launches += step(i)
+    else:
+        with torch.cuda.stream(stream):
+            for g in graphs:
+                g.replay()
+        launches = args.steps * len(launches_per_set[0])
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end)
@@ -734,7 +849,9 @@ def main():
                                f"{args.mode} mode ({rows} rows), eps={wl.eps}",
                    "num_tokens": T, "hidden": h, "num_partials": N, "storage_dtype": wl.dtype,
                    "mode": args.mode, "rows": rows, "rotated_input_sets": R,
-                   "launches_per_step": launches / args.steps},
+                   "launches_per_step": launches / args.steps,
+                   "launch": ("hip graph replays, one graph per %d-step rotation cycle" % R
+                              if args.graph else "eager stream launches")},
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(rows / (ms_per_step * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
@@ -753,6 +870,8 @@ def main():
         result["split_table"] = split_table
     if cu_mask is not None:
         result["cu_mask"] = cu_mask
+    if ramp is not None:
+        result["ramp"] = ramp
     if staircase is not None:
         result["gemm_staircase"] = staircase
     if ceiling is not None:

@@ -12,7 +12,8 @@
 //
 // A third kind of probe records where each workgroup ran (XCC and compute unit
 // as the hardware reports them), which shows how a stream's CU mask maps onto
-// the eight XCDs.
+// the eight XCDs.  A fourth does nothing at all: back-to-back launches of it
+// measure the fixed cost of a dependent launch of a given grid.
 
 #include <hip/hip_runtime.h>
 
@@ -116,17 +117,29 @@ constexpr std::array<ProbeFn, sizeof...(Ks)> r_table(std::integer_sequence<int, 
 const auto kReadWrite = rw_table(std::make_integer_sequence<int, kMaxStreams>{});
 const auto kRead = r_table(std::make_integer_sequence<int, kMaxStreams>{});
 
+// No memory access and no work: 1024 threads per workgroup, as the fused
+// kernel's widest rows use.
+constexpr int kEmptyBlock = 1024;
+__global__ __launch_bounds__(kEmptyBlock) void probe_empty(ProbeArgs) {}
+
 }  // namespace
 
 // kind 0: read+write, 1: read only, 2: write only, 3: placement (one 16-byte
-// record per workgroup into dst[0], which must hold at least grid vectors).
+// record per workgroup into dst[0], which must hold at least grid vectors),
+// 4: empty (grid workgroups of 1024 threads; no tensor is touched).
 // Returns 0 or a HIP error code; -1 for arguments out of range.  nvec counts
 // 16-byte vectors per tensor.
 extern "C" int tw_probe_launch(int kind, const void* const* src, int nsrc, void* const* dst,
                                int ndst, int64_t nvec, int grid, void* stream) {
-  if (kind < 0 || kind > 3 || nsrc < 0 || nsrc > kMaxStreams || ndst < 0 || ndst > kMaxStreams ||
+  if (kind < 0 || kind > 4 || nsrc < 0 || nsrc > kMaxStreams || ndst < 0 || ndst > kMaxStreams ||
       nvec < 1 || grid < 1 || grid > 65536)
     return -1;
+  if (kind == 4) {
+    ProbeArgs e{};
+    void* eargs[] = {&e};
+    return (int)hipLaunchKernel((const void*)&probe_empty, dim3(grid), dim3(kEmptyBlock), eargs,
+                                0, static_cast<hipStream_t>(stream));
+  }
   if (kind == 3) {
     if (ndst != 1 || dst[0] == nullptr || nvec < grid) return -1;
     ProbeArgs p{};
