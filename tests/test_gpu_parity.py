@@ -86,19 +86,26 @@ def test_shard_mode_matches_full_and_leaves_other_rows(name):
         assert np.isnan(canary).all()
 
 
-def test_split_launches_equal_one_launch_for_every_offset():
-    d = make_inputs("qwen72b")
-    T = d["workload"].num_tokens
+# The planner settings the benchmark uses for each workload: 256 x 256 GEMM
+# tiles across h, one per CU on 256 CUs; the MoE threshold for mixtral.
+SPLIT_PLANS = {"qwen72b": 1024, "mixtral": 4096, "llama405b": 1024}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_PLANS))
+def test_split_launches_equal_one_launch_for_every_offset(name):
+    d = make_inputs(name)
+    T, h = d["workload"].num_tokens, d["workload"].hidden
     parts, res, w = upload(d)
-    say("full qwen72b (reference for splits)")
+    say(f"full {name} (reference for splits)")
     out_full, rout_full = _run_full(parts, res, w, d["eps"])
-    plan = tw.tw_split_plan(T, tokens_per_cta=256, ctas_per_token_tile=32, num_cus=256,
-                            min_split_tokens=1024)
-    assert plan == oracle.split_plan(T, tokens_per_cta=256, ctas_per_token_tile=32, num_cus=256,
-                                     min_split_tokens=1024)
+    kw = dict(tokens_per_cta=256, ctas_per_token_tile=h // 256, num_cus=256,
+              min_split_tokens=SPLIT_PLANS[name])
+    plan = tw.tw_split_plan(T, **kw)
+    assert plan == oracle.split_plan(T, **kw)
+    assert plan["reason"] == 0           # the benchmark's step is this split
     prefixes = sorted({T // 2 + off for off in oracle.DEFAULT_OFFSETS} | {plan["prefix_tokens"]})
     for P in prefixes:
-        say(f"split qwen72b prefix={P} suffix={T - P}")
+        say(f"split {name} prefix={P} suffix={T - P}")
         out, rout = tw.tw_fused_reduce_rmsnorm_split(parts, res, w, d["eps"], P)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(to_host(out), out_full)
