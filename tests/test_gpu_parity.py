@@ -328,6 +328,49 @@ def test_captured_split_step_replays_match_eager():
         _ = torch.ones(1000, device="cuda").sum().item()      # eager work between replays
 
 
+def test_graph_replayed_fused_launches_match_eager():
+    # The benchmark's graph mode: prepared full, shard and split launches on
+    # rotated buffer sets, recorded into one HIP graph on a side stream.  Every
+    # replay, with the outputs cleared and eager work in between, must give
+    # the eager launches' bits.
+    T, h, R = 320, 8192, 3
+    d = make_inputs("llama70b", num_tokens=T, hidden=h)
+    parts, res, w = upload(d)
+    ref_out, ref_rout = _run_full(parts, res, w, d["eps"])
+    sets = [(parts.clone(), res.clone(), torch.empty_like(res), torch.empty_like(res))
+            for _ in range(R)]
+    cap = torch.cuda.Stream()
+    P = 192
+    launches = []
+    for i, (p, r, o, ro) in enumerate(sets):
+        if i == 0:
+            launches.append(tw.PreparedFused(p, r, w, d["eps"], o, ro, cap))
+        elif i == 1:
+            launches += [tw.PreparedFused([q[lo:hi] for q in p], r[lo:hi], w, d["eps"], o[lo:hi],
+                                          ro[lo:hi], cap) for lo, hi in ((0, P), (P, T))]
+        else:
+            launches += [tw.PreparedFused(p, r, w, d["eps"], o, ro, cap, mode="shard",
+                                          shard_index=k) for k in range(8)]
+    say("capture full, split and shard launches into one graph")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for launch in launches:
+            launch()
+    for rep in range(4):
+        for _, _, o, ro in sets:
+            o.fill_(float("nan"))
+            ro.fill_(float("nan"))
+        torch.cuda.synchronize()
+        say(f"graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for _, _, o, ro in sets:
+            np.testing.assert_array_equal(to_host(o), ref_out)
+            np.testing.assert_array_equal(to_host(ro), ref_rout)
+        _ = torch.ones(1000, device="cuda").sum().item()      # eager work between replays
+
+
 def test_prepared_launches_match_direct_calls():
     d = make_inputs("llama70b", num_tokens=96, hidden=8192)
     parts, res, w = upload(d)
