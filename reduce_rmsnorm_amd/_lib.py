@@ -231,8 +231,9 @@ def tw_reduce_partials(partials, reduced: Optional[torch.Tensor] = None,
     if ref.dim() != 2:
         raise ValueError("partials must be [T, h]")
     for p in parts:
-        if not p.is_cuda or p.dtype != ref.dtype or not p.is_contiguous() or p.shape != ref.shape:
-            raise ValueError("partials must be contiguous GPU tensors of one shape and dtype")
+        if not p.is_cuda or p.dtype != ref.dtype or not p.is_contiguous() or p.shape != ref.shape \
+                or p.device != ref.device:
+            raise ValueError("partials must be contiguous tensors of one shape and dtype on one GPU")
     if reduced is None:
         reduced = torch.empty_like(ref)
     if reduced.shape != ref.shape or reduced.dtype != ref.dtype or not reduced.is_contiguous() \
@@ -369,6 +370,8 @@ class SplitPlanCache:
         self._plans = {}
 
     def __call__(self, num_tokens: int) -> dict:
+        """The plan for ``num_tokens`` (a copy: changing it leaves the table
+        alone)."""
         plan = self._plans.get(num_tokens)
         if plan is None:
             plan = tw_split_plan(num_tokens, **self._problem)
@@ -383,7 +386,7 @@ class SplitPlanCache:
                     plan.update(prefix_tokens=prefix, suffix_tokens=num_tokens - prefix,
                                 offset=off, reason=TW_PLAN_SPLIT)
             self._plans[num_tokens] = plan
-        return plan
+        return dict(plan)
 
 
 def split_table_from_sweep(rows) -> dict:

@@ -27,7 +27,8 @@ constexpr int32_t kDefaultOffsets[] = {0, 64, 128, 192, 256, 512};
 constexpr int64_t kMaxTokens = int64_t(1) << 40;
 constexpr int64_t kMaxTiles = int64_t(1) << 20;
 
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// a >= 0, b >= 1; no intermediate can overflow, whatever b is.
+int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0 ? 1 : 0); }
 
 struct WaveModel {
   int64_t tokens_per_cta, tiles, slots;

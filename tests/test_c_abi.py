@@ -48,7 +48,11 @@ def cases():
     rnd = random.Random(5)
     c = [(257, 1, 1, 256, 1, 0), (514, 1, 1, 256, 1, 0), (300, 1, 1, 132, 1, 0),
          (393, 1, 1, 132, 1, 0), (0, 1, 1, 256, 1, 0), (100, 1, 1, 256, 1, 1024),
-         (4096, 256, 32, 256, 1, 1024), (8192, 256, 16, 256, 1, 4096)]
+         (4096, 256, 32, 256, 1, 1024), (8192, 256, 16, 256, 1, 4096),
+         # extreme tile models: no wave arithmetic may overflow int64 on the way
+         (2 ** 40, 2 ** 63 - 1, 1, 256, 1, 0), (5000, 2 ** 63 - 1, 2 ** 20, 1, 1, 0),
+         (2 ** 40, 1, 1, 2 ** 31 - 1, 2 ** 31 - 1, 0), (2 ** 40, 2 ** 62, 2 ** 20, 2 ** 31 - 1, 1, 0),
+         (70000, 2 ** 63 - 1, 64, 256, 4, 1024)]
     for _ in range(300):
         c.append((rnd.randint(0, 70000), rnd.choice([1, 64, 128, 256]), rnd.randint(1, 64),
                   rnd.choice([132, 256, 304]), rnd.randint(1, 4), rnd.choice([0, 1024, 4096])))
