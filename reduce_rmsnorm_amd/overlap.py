@@ -35,6 +35,8 @@ from typing import Optional, Sequence
 
 import torch
 
+from ._lib import tw_fused_reduce_rmsnorm, tw_fused_reduce_rmsnorm_grid
+
 NUM_MASK_BITS = 256
 
 
@@ -43,7 +45,15 @@ def _hip_runtime() -> ctypes.CDLL:
     # that same instance, so streams made here are usable by torch and by this
     # library's launches.
     torch.cuda.init()
-    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip = None
+    for name in ("libamdhip64.so.7", "libamdhip64.so"):
+        try:
+            hip = ctypes.CDLL(name)
+            break
+        except OSError:
+            continue
+    if hip is None:
+        raise RuntimeError("the HIP runtime library (libamdhip64.so) is not loadable")
     hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
                                                  ctypes.POINTER(ctypes.c_uint32)]
     hip.hipExtStreamCreateWithCUMask.restype = ctypes.c_int
@@ -106,8 +116,6 @@ class MaskedStream:
 
     def __exit__(self, *exc):
         self.close()
-
-from ._lib import tw_fused_reduce_rmsnorm, tw_fused_reduce_rmsnorm_grid
 
 
 class LayerStep:
