@@ -34,6 +34,11 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFORM
 
 HOST_SOURCES = ["api.cpp", "split_plan.cpp"]
 HIP_SOURCES = ["fused_reduce_rmsnorm.hip", "unfused.hip"]
+# Per-source flags.  The fused one-row kernel takes its first three arguments
+# (first tensor, first row, row length) as scalars for the hardware to preload
+# into SGPRs at wave launch, so a wave's first load need not wait for the
+# argument block.
+HIP_SOURCE_FLAGS = {"fused_reduce_rmsnorm.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=3"]}
 # Measurement-only bandwidth probes (bench.py --ceiling, counter calibration),
 # built into a library of their own so the fused library carries none of them.
 PROBE_SOURCE = "bw_probe.hip"
@@ -75,7 +80,8 @@ def build(verbose: bool = False) -> str:
         objs.append(obj)
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        cmds.append([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src),
+        cmds.append([hipcc, *HIP_FLAGS, *HIP_SOURCE_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC,
+                     "-c", os.path.join(CSRC, src),
                      "-o", obj])
         objs.append(obj)
     if verbose:

@@ -43,6 +43,13 @@
 //  * Partials and residual are streamed with non-temporal loads, the outputs
 //    with non-temporal stores; the weight row (read by every workgroup) uses
 //    ordinary loads so it stays in L2.
+//  * The one-row-per-workgroup kernel takes the first tensor's address, the
+//    first row and the row length as leading scalar arguments, which this
+//    file's build preloads into SGPRs at wave launch (kernel-argument
+//    preloading, -mllvm -amdgpu-kernarg-preload-count=3).  A wave issues its
+//    row's first load at once; the rest of the argument block (the other
+//    tensors' addresses, the weight) arrives from memory while that load is in
+//    flight.
 
 #include <hip/hip_runtime.h>
 
@@ -73,7 +80,8 @@ struct KArgs {
 };
 
 // Tensor I of the summation: partial I for I < N, the residual for I == N.
-#define TW_TENSOR(I) ((I) < N ? a.partials[(I) < N ? (I) : 0] : a.residual)
+// Partial 0 is k_first, the kernel's own (preloaded) copy of its address.
+#define TW_TENSOR(I) ((I) == 0 ? k_first : (I) < N ? a.partials[(I) < N ? (I) : 0] : a.residual)
 
 // Finishing one vector slot J from its compensated pair (S, C): x, the stored
 // residual (correctly rounded for bf16) and the slot's share of the sum of
@@ -95,7 +103,8 @@ _Pragma("unroll")                                                               
 
 // The per-row body of both fused kernels: everything the fused step does to
 // the row ROW_EXPR, by one workgroup, with the wave partial sums in the LDS
-// array wave_part[BLOCK / 64] and E, NW in scope.  Written once and expanded
+// array wave_part[BLOCK / 64], E, NW, k_first (partial 0) and k_nvec (16-byte
+// vectors per row) in scope.  Written once and expanded
 // into each kernel, so that both compile it in a kernel's own context (an
 // inlined device function allocated registers differently and spilled).
 //
@@ -106,12 +115,14 @@ _Pragma("unroll")                                                               
 //  * SEQ == D > 0: the tensors are loaded in summation order, D of them in
 //    flight: tensor i + D is requested once tensor i has been added.  Fewer
 //    DRAM regions are open at a time across the chip, which streams faster
-//    when there are many partials.
+//    when there are many partials.  The first loads go out before anything
+//    else; the other tensors' addresses and the weight row are fetched while
+//    they are in flight (scheduling barriers keep that order).
 #define TW_FUSED_ROW_BODY(ROW_EXPR)                                                    \
   const int tid = threadIdx.x;                                                         \
   const int64_t row = (ROW_EXPR);                                                      \
-  const int64_t base = row * (int64_t)a.nvec;                                          \
-  const int nvec = a.nvec;                                                             \
+  const int64_t base = row * (int64_t)k_nvec;                                          \
+  const int nvec = k_nvec;                                                             \
                                                                                        \
   int vi[VPT];                                                                         \
   bool valid[VPT];                                                                     \
@@ -123,7 +134,7 @@ _Pragma("unroll")                                                               
   }                                                                                    \
                                                                                        \
   u32x4 wraw[VPT];                                                                     \
-  if constexpr (CHUNK == VPT) {                                                        \
+  if constexpr (CHUNK == VPT && SEQ == 0) {                                            \
 _Pragma("unroll")                                                                      \
     for (int j = 0; j < VPT; ++j) wraw[j] = a.weight[vi[j]];                           \
   }                                                                                    \
@@ -132,6 +143,7 @@ _Pragma("unroll")                                                               
   float x[VPT][E];                                                                     \
   float ss = 0.0f;                                                                     \
   if constexpr (SEQ > 0) {                                                             \
+    const u32x4* tp[N + 1];                                                            \
 _Pragma("unroll")                                                                      \
     for (int j0 = 0; j0 < VPT; j0 += CHUNK) {                                          \
       u32x4 raw[N + 1][CHUNK];                                                         \
@@ -141,6 +153,16 @@ _Pragma("unroll")                                                               
 _Pragma("unroll")                                                                      \
         for (int jj = 0; jj < CHUNK; ++jj)                                             \
           raw[i][jj] = __builtin_nontemporal_load(TW_TENSOR(i) + base + vi[j0 + jj]);  \
+      __builtin_amdgcn_sched_barrier(0);                                               \
+      if (j0 == 0) {                                                                   \
+_Pragma("unroll")                                                                      \
+        for (int i = 0; i <= N; ++i) tp[i] = TW_TENSOR(i);                             \
+        if (CHUNK == VPT) {                                                            \
+_Pragma("unroll")                                                                      \
+          for (int j = 0; j < VPT; ++j) wraw[j] = a.weight[vi[j]];                     \
+        }                                                                              \
+      }                                                                                \
+      __builtin_amdgcn_sched_barrier(0);                                               \
 _Pragma("unroll")                                                                      \
       for (int i = 0; i <= N; ++i) {                                                   \
         __builtin_amdgcn_sched_barrier(0);                                             \
@@ -162,7 +184,8 @@ _Pragma("unroll")                                                               
 _Pragma("unroll")                                                                      \
           for (int jj = 0; jj < CHUNK; ++jj)                                           \
             raw[i + SEQ <= N ? i + SEQ : N][jj] =                                      \
-                __builtin_nontemporal_load(TW_TENSOR(i + SEQ) + base + vi[j0 + jj]);   \
+                __builtin_nontemporal_load(tp[i + SEQ <= N ? i + SEQ : N] + base +      \
+                                           vi[j0 + jj]);                               \
         }                                                                              \
       }                                                                                \
 _Pragma("unroll")                                                                      \
@@ -176,7 +199,7 @@ _Pragma("unroll")                                                               
       for (int i = 0; i < N; ++i)                                                      \
 _Pragma("unroll")                                                                      \
         for (int jj = 0; jj < CHUNK; ++jj)                                             \
-          raw[i][jj] = __builtin_nontemporal_load(a.partials[i] + base + vi[j0 + jj]); \
+          raw[i][jj] = __builtin_nontemporal_load(TW_TENSOR(i) + base + vi[j0 + jj]);  \
 _Pragma("unroll")                                                                      \
       for (int jj = 0; jj < CHUNK; ++jj)                                               \
         raw[N][jj] = __builtin_nontemporal_load(a.residual + base + vi[j0 + jj]);      \
@@ -221,14 +244,17 @@ _Pragma("unroll")                                                               
     if (valid[j]) __builtin_nontemporal_store(pack<BF16>(y), a.out + base + vi[j]);    \
   }
 
-// One workgroup per row: the launch grid is the row count.
+// One workgroup per row: the launch grid is the row count.  k_first,
+// k_row_begin and k_nvec repeat a.partials[0], a.row_begin and a.nvec as
+// preloaded scalar arguments.
 template <int N, int BLOCK, int VPT, bool BF16, int WPE, int CHUNK, int SEQ>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(WPE)))
-void fused_reduce_rmsnorm_kernel(KArgs a) {
+void fused_reduce_rmsnorm_kernel(const u32x4* k_first, int64_t k_row_begin, int32_t k_nvec,
+                                 KArgs a) {
   constexpr int E = Elem<BF16>::kPerVec;
   constexpr int NW = BLOCK / 64;
   __shared__ float wave_part[NW];
-  TW_FUSED_ROW_BODY(a.row_begin + blockIdx.x)
+  TW_FUSED_ROW_BODY(k_row_begin + blockIdx.x)
 }
 
 // A fixed number of workgroups: workgroup b takes the consecutive rows
@@ -244,6 +270,8 @@ __global__ __launch_bounds__(BLOCK) void fused_reduce_rmsnorm_rows_kernel(KArgs 
   constexpr int E = Elem<BF16>::kPerVec;
   constexpr int NW = BLOCK / 64;
   __shared__ float wave_part[NW];
+  const u32x4* const k_first = a.partials[0];
+  const int32_t k_nvec = a.nvec;
   const int64_t first = a.row_begin + (int64_t)blockIdx.x * rows_per_wg;
   const int64_t last = first + rows_per_wg < row_end ? first + rows_per_wg : row_end;
   for (int64_t r = first; r < last; ++r) {
@@ -252,7 +280,7 @@ __global__ __launch_bounds__(BLOCK) void fused_reduce_rmsnorm_rows_kernel(KArgs 
   }
 }
 
-using KernelFn = void (*)(KArgs);
+using KernelFn = void (*)(const u32x4*, int64_t, int32_t, KArgs);
 using RowsKernelFn = void (*)(KArgs, int64_t, int64_t);
 
 // Kernel tables by [row class][N - 1].  SEQ_ORDER selects the geometry's own
@@ -339,7 +367,10 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
     for (int64_t r0 = 0; r0 < L.num_rows && e == hipSuccess; r0 += chunk) {
       const int64_t n = L.num_rows - r0 < chunk ? L.num_rows - r0 : chunk;
       k.row_begin = L.row_begin + r0;
-      void* args[] = {&k};
+      const u32x4* first = k.partials[0];
+      int64_t row_begin = k.row_begin;
+      int32_t nvec32 = k.nvec;
+      void* args[] = {&first, &row_begin, &nvec32, &k};
       e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)n), dim3(block), args,
                           0, static_cast<hipStream_t>(L.stream));
     }

@@ -45,12 +45,13 @@ PROBE_READ = "probe_read<"
 PROBE_WRITE = "probe_write("
 
 
-def kernel_code_hash(paths=None) -> str:
+def kernel_code_hash(paths=None, flags=None) -> str:
     """SHA-256 of the fused kernel's code with comments and whitespace
-    removed: counters taken on one version stay attached to it through
-    comment edits, and any change to the code itself (kernel, geometry table,
-    device helpers) gives a new hash.  (The sources hold no string literal
-    containing comment markers.)"""
+    removed, and of the flags it is compiled with: counters taken on one
+    version stay attached to it through comment edits, and any change to the
+    code itself (kernel, geometry table, device helpers) or to its compile
+    flags gives a new hash.  (The sources hold no string literal containing
+    comment markers.)"""
     h = hashlib.sha256()
     for path in paths or KERNEL_SOURCES:
         text = open(path, encoding="utf-8").read()
@@ -58,6 +59,10 @@ def kernel_code_hash(paths=None) -> str:
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(os.path.basename(path).encode())
         h.update(" ".join(text.split()).encode())
+    if flags is None:
+        from reduce_rmsnorm_amd.build import HIP_FLAGS, HIP_SOURCE_FLAGS
+        flags = HIP_FLAGS + HIP_SOURCE_FLAGS.get(os.path.basename(KERNEL_SOURCES[0]), [])
+    h.update(" ".join(flags).encode())
     return h.hexdigest()
 
 

@@ -33,5 +33,11 @@ def test_kernel_code_hash_ignores_comments_and_catches_code(tmp_path):
     assert kernel_code_hash(copies) != base                 # a code change
     k.write_text(text)
     g = tmp_path / "geometry.h"
-    g.write_text(g.read_text().replace("{512, 2, 6, 2, 0}", "{512, 2, 5, 2, 0}"))
+    geo = g.read_text()
+    g.write_text(geo.replace("{512, 2, 6, 2, 0}", "{512, 2, 5, 2, 0}"))
     assert kernel_code_hash(copies) != base                 # the geometry table is code too
+    g.write_text(geo)
+    from reduce_rmsnorm_amd.build import HIP_FLAGS, HIP_SOURCE_FLAGS
+    flags = HIP_FLAGS + HIP_SOURCE_FLAGS["fused_reduce_rmsnorm.hip"]
+    assert kernel_code_hash(copies, flags) == base
+    assert kernel_code_hash(copies, HIP_FLAGS) != base      # so are its compile flags

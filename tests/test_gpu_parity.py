@@ -391,8 +391,9 @@ def test_prepared_launches_match_direct_calls():
                               min_split_tokens=1024)
     assert cache(4096) == oracle.split_plan(4096, tokens_per_cta=256, ctas_per_token_tile=32,
                                             num_cus=256, min_split_tokens=1024)
-    assert cache(4096) is cache(4096)
-
+    plan = cache(4096)
+    plan["offset"] = 99
+    assert cache(4096)["offset"] == 0                      # cached plans are handed out as copies
 
 
 @pytest.mark.parametrize("N", list(range(1, 17)))
