@@ -109,6 +109,9 @@ def parse():
                     help="also run the fused kernel on CU-masked streams: where mask bits land "
                          "(XCD, CU), GB/s against the number of CUs, and the split layer step "
                          "with the fused kernel and the GEMM on disjoint CU sets")
+    ap.add_argument("--launch-floor", action="store_true",
+                    help="also time an empty kernel of 1, 256, 1024 and 4096 workgroups, "
+                         "replayed from a HIP graph: the fixed cost of a dependent launch")
     ap.add_argument("--ceiling", action="store_true",
                     help="also time the bandwidth probes on the same buffers: N+1 streamed reads "
                          "+ 2 streamed writes, reads only, writes only (the achievable envelope; "
@@ -172,14 +175,20 @@ def run_ceiling(sets, R, rows, h, itemsize, stream, steps, timer):
         res[key + "_gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
         print(f"[bench] probe {key}: {nbytes} B in {us:.2f} us = {res[key + '_gbs']} GB/s",
               file=sys.stderr, flush=True)
+    return res
 
-    # The fixed cost of one dependent launch: an empty kernel of G workgroups
-    # of 1024 threads, EMPTY_LAUNCHES of them recorded in a HIP graph and
-    # replayed (eager launches this short would time the host instead).
-    import torch
+
+def run_launch_floor(torch, timer) -> dict:
+    """The fixed cost of one dependent launch: an empty kernel of G
+    workgroups of 1024 threads, EMPTY_LAUNCHES of them recorded in a HIP graph
+    and replayed (eager launches this short would time the host instead).
+    Kept apart from the stream probes: the counter passes run those, and HIP
+    graph capture under rocprofv3 --pmc ends the profiler."""
+    import ctypes
+    lib = _probe_lib()
     cap = torch.cuda.Stream()
     none = (ctypes.c_void_p * 1)()
-    res["empty_launch_us"] = {}
+    res = {}
     for grid in (1, 256, 1024, 4096):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
@@ -190,7 +199,7 @@ def run_ceiling(sets, R, rows, h, itemsize, stream, steps, timer):
         for _ in range(100):            # capture idled the GPU: settle it again first
             g.replay()
         us = timer(lambda i, g=g: g.replay(), 20) / EMPTY_LAUNCHES
-        res["empty_launch_us"][str(grid)] = round(us, 3)
+        res[str(grid)] = round(us, 3)
         print(f"[bench] empty kernel, {grid} workgroups of 1024 threads: {us:.2f} us per launch "
               f"(graph replay)", file=sys.stderr, flush=True)
         del g
@@ -809,21 +818,25 @@ def main():
         overlap = run_overlap(tw, torch, wl, plan_kw,
                               [int(t) for t in args.overlap_tokens.split(",")], args.overlap_lean)
 
+    def timer(go, k):
+        for i in range(min(20, k)):
+            go(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(k):
+            go(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / k
+
     ceiling = None
     if args.ceiling:
-        def timer(go, k):
-            for i in range(min(20, k)):
-                go(i)
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(k):
-                go(i)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) * 1e3 / k
         ceiling = run_ceiling(sets, R, rows, h, wl.itemsize, stream, min(args.steps, 500), timer)
+    launch_floor = None
+    if args.launch_floor:
+        launch_floor = run_launch_floor(torch, timer)
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE) and args.mode == "full" and wl.name == "llama70b":
@@ -872,6 +885,8 @@ def main():
         result["cu_mask"] = cu_mask
     if ramp is not None:
         result["ramp"] = ramp
+    if launch_floor is not None:
+        result["empty_launch_us"] = launch_floor
     if staircase is not None:
         result["gemm_staircase"] = staircase
     if ceiling is not None:

@@ -168,7 +168,8 @@ def traffic(fetch: str, write: str, workload: str, cmd_fetch: str, cmd_write: st
           f"Traffic / algorithmic bytes = {res['traffic_over_algorithmic']:.5f} "
           "(the weight row, 16 KiB, is fetched by each XCD's L2 and is not in the "
           "algorithmic count).", "",
-          f"Kernel code sha256 (comments and whitespace removed; kernel source and headers): `{res['kernel_code_sha256']}`"]
+          f"Kernel code sha256 (kernel source and headers with comments and whitespace removed, "
+          f"and the compile flags): `{res['kernel_code_sha256']}`"]
     with open(out + ".md", "w") as f:
         f.write("\n".join(md) + "\n")
     print(json.dumps(res, indent=1))
