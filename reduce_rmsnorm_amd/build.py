@@ -35,10 +35,12 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFORM
 HOST_SOURCES = ["api.cpp", "split_plan.cpp"]
 HIP_SOURCES = ["fused_reduce_rmsnorm.hip", "unfused.hip"]
 # Per-source flags.  The fused one-row kernel takes its first three arguments
-# (first tensor, first row, row length) as scalars for the hardware to preload
+# (first tensor, first row, row length), the comparator's reduce kernel its
+# first two (first tensor, row length), as scalars for the hardware to preload
 # into SGPRs at wave launch, so a wave's first load need not wait for the
 # argument block.
-HIP_SOURCE_FLAGS = {"fused_reduce_rmsnorm.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=3"]}
+HIP_SOURCE_FLAGS = {"fused_reduce_rmsnorm.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=3"],
+                    "unfused.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"]}
 # Measurement-only bandwidth probes (bench.py --ceiling, counter calibration),
 # built into a library of their own so the fused library carries none of them.
 PROBE_SOURCE = "bw_probe.hip"

@@ -55,14 +55,19 @@ struct AddNormArgs {
 // The reduce step uses the fused kernel's row geometry and load orders (all
 // loads of CHUNK slots at once, or the partials in summation order with SEQ in
 // flight), so that the comparator streams as well as the fused kernel does.
-// No value is shared between threads, so the geometry never changes a bit.
+// Like the fused kernel it takes partial 0's address and the row length as
+// leading scalar arguments (k_first, k_nvec: copies of a.partials[0] and
+// a.nvec) that this file's build preloads into SGPRs, so a wave's first load
+// does not wait for the argument block.  No value is shared between threads,
+// so the geometry never changes a bit.
 template <int N, int BLOCK, int VPT, bool BF16, int WPE, int CHUNK, int SEQ>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(WPE)))
-void reduce_kernel(ReduceArgs a) {
+void reduce_kernel(const u32x4* k_first, int32_t k_nvec, ReduceArgs a) {
   constexpr int E = Elem<BF16>::kPerVec;
   const int tid = threadIdx.x;
-  const int64_t base = (int64_t)blockIdx.x * a.nvec;
-  const int nvec = a.nvec;
+  const int64_t base = (int64_t)blockIdx.x * k_nvec;
+  const int nvec = k_nvec;
+  const u32x4* tp[N];
   int vi[VPT];
   bool valid[VPT];
 #pragma unroll
@@ -80,13 +85,23 @@ void reduce_kernel(ReduceArgs a) {
       for (int i = 0; i < SEQ && i < N; ++i)
 #pragma unroll
         for (int jj = 0; jj < CHUNK; ++jj)
-          raw[i][jj] = __builtin_nontemporal_load(a.partials[i] + base + vi[j0 + jj]);
+          raw[i][jj] = __builtin_nontemporal_load((i == 0 ? k_first : a.partials[i]) + base +
+                                                  vi[j0 + jj]);
+      // The other partials' addresses arrive while the first loads are in
+      // flight.
+      __builtin_amdgcn_sched_barrier(0);
+      if (j0 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) tp[i] = i == 0 ? k_first : a.partials[i];
+      }
+      __builtin_amdgcn_sched_barrier(0);
     } else {
 #pragma unroll
       for (int i = 0; i < N; ++i)
 #pragma unroll
         for (int jj = 0; jj < CHUNK; ++jj)
-          raw[i][jj] = __builtin_nontemporal_load(a.partials[i] + base + vi[j0 + jj]);
+          raw[i][jj] = __builtin_nontemporal_load((i == 0 ? k_first : a.partials[i]) + base +
+                                                  vi[j0 + jj]);
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -110,7 +125,7 @@ void reduce_kernel(ReduceArgs a) {
 #pragma unroll
           for (int jj = 0; jj < CHUNK; ++jj)
             raw[i + SEQ < N ? i + SEQ : N - 1][jj] = __builtin_nontemporal_load(
-                a.partials[i + SEQ < N ? i + SEQ : N - 1] + base + vi[j0 + jj]);
+                tp[i + SEQ < N ? i + SEQ : N - 1] + base + vi[j0 + jj]);
         }
       }
     }
@@ -190,7 +205,7 @@ __global__ __launch_bounds__(BLOCK) void add_rmsnorm_kernel(AddNormArgs a) {
   }
 }
 
-using ReduceFn = void (*)(ReduceArgs);
+using ReduceFn = void (*)(const u32x4*, int32_t, ReduceArgs);
 using AddNormFn = void (*)(AddNormArgs);
 
 constexpr int reduce_order(int g, int n, bool seq_order) {
@@ -258,7 +273,9 @@ int launch_reduce(const ReduceLaunch& L, char* err, size_t errlen) {
     ReduceArgs kc = k;
     for (int i = 0; i < L.num_partials; ++i) kc.partials[i] = k.partials[i] + r0 * nvec;
     kc.reduced = k.reduced + r0 * nvec;
-    void* args[] = {&kc};
+    const u32x4* first = kc.partials[0];
+    int32_t nvec32 = kc.nvec;
+    void* args[] = {&first, &nvec32, &kc};
     e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)n),
                         dim3(geo.block), args, 0, static_cast<hipStream_t>(L.stream));
   }
