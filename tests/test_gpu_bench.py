@@ -1,0 +1,48 @@
+"""bench.py's JSON line on a GPU: a short run must keep the contract (one
+line, the metric and units, the roofline and CPU-oracle objects, and a value
+consistent with its own step time and byte count)."""
+
+from __future__ import annotations
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("mode", ["full", "shard"])
+def test_bench_line_keeps_the_contract(mode):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    print(f"[case] bench.py --mode {mode} --steps 40 --warmup 10", flush=True)
+    run = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--mode", mode,
+                          "--steps", "40", "--warmup", "10", "--cpu-seconds", "0.5",
+                          "--no-unfused"], capture_output=True, text=True, timeout=240)
+    assert run.returncode == 0, run.stderr[-2000:]
+    lines = [ln for ln in run.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline"):
+        assert key in d, key
+    assert d["unit"] == "GB/s" and d["n_gpus"] == 1 and d["steps"] == 40 and d["warmup"] == 10
+    assert d["higher_is_better"] is True and d["vs_baseline"] is None
+    cfg = d["config"]
+    rows = cfg["rows"]
+    assert rows == (1024 if mode == "full" else 128)
+    step_bytes = (cfg["num_partials"] + 3) * rows * cfg["hidden"] * 2
+    assert abs(d["value"] - step_bytes / (d["ms_per_step"] * 1e-3) / 1e9) <= 0.01 * d["value"]
+    r = d["roofline"]
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
+    assert abs(r["frac"] - d["value"] / 8000.0) < 1e-3
+    assert 0 < r["frac"] < 1
+    c = d["cpu_baseline"]
+    assert c["kind"] == "oracle" and c["cores"] == 1 and c["value"] > 0
