@@ -73,6 +73,12 @@ def parse():
                          "the ramp that the warm-up covers" % (RAMP_BLOCKS * RAMP_BLOCK,
                                                                      RAMP_BLOCK))
     ap.add_argument("--workload", default="llama70b")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="override the workload's token count T (same distributions)")
+    ap.add_argument("--partials", type=int, default=None,
+                    help="override the workload's partial count N (same distributions)")
+    ap.add_argument("--no-split", dest="split", action="store_false",
+                    help="keep every batch whole (one launch per step) whatever the planner says")
     ap.add_argument("--mode", choices=("full", "shard"), default="full",
                     help="full: every row; shard: shard 0's rows (one rank's share)")
     ap.add_argument("--rotate", type=int, default=0,
@@ -589,6 +595,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = WORKLOADS[args.workload]
+    overridden = args.tokens is not None or args.partials is not None
+    if overridden:
+        import dataclasses
+        wl = dataclasses.replace(wl, num_tokens=args.tokens or wl.num_tokens,
+                                 num_partials=args.partials or wl.num_partials)
     T, h, N = wl.num_tokens, wl.hidden, wl.num_partials
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
 
@@ -628,6 +639,8 @@ def main():
     # prepared once per rotated buffer set so the host costs one C call each.
     planner = tw.SplitPlanCache(**plan_kw)
     plan0 = planner(T)
+    if not args.split and plan0["reason"] == 0:
+        plan0 = dict(plan0, prefix_tokens=T, suffix_tokens=0, offset=-1, reason=-1)
     def prepare(st):
         per_set = []
         for parts, res, out, rout in sets:
@@ -646,7 +659,7 @@ def main():
     launches_per_set = prepare(stream)
 
     def step(i):
-        plan = planner(T) if args.mode == "full" else None
+        plan = planner(T) if args.mode == "full" and args.split else None
         assert plan is None or plan["prefix_tokens"] == plan0["prefix_tokens"]
         for launch in launches_per_set[i % R]:
             launch()
@@ -839,7 +852,8 @@ def main():
         launch_floor = run_launch_floor(torch, timer)
 
     traffic = None
-    if os.path.exists(TRAFFIC_FILE) and args.mode == "full" and wl.name == "llama70b":
+    if os.path.exists(TRAFFIC_FILE) and args.mode == "full" and wl.name == "llama70b" \
+            and not overridden:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("kernel_code_sha256") == kernel_source_hash():

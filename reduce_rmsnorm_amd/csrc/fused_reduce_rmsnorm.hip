@@ -362,7 +362,12 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
   if (L.max_workgroups <= 0 || L.max_workgroups >= L.num_rows) {
     const bool seq = L.num_rows >= seq_min_workgroups(block);
     const KernelFn fn = kTable[bf16][seq][g][L.num_partials - 1];
-    const int64_t chunk = max_rows_per_dispatch(block);
+    // Dispatches over consecutive row ranges of about equal size, each within
+    // the byte and work-item limits; the per-row code is the same in each.
+    const int64_t row_bytes = (int64_t)(L.num_partials + 3) * nvec * 16;
+    const int64_t cap = fused_rows_per_dispatch(block, row_bytes, seq_min_workgroups(block));
+    const int64_t pieces = (L.num_rows + cap - 1) / cap;
+    const int64_t chunk = (L.num_rows + pieces - 1) / pieces;
     e = hipSuccess;
     for (int64_t r0 = 0; r0 < L.num_rows && e == hipSuccess; r0 += chunk) {
       const int64_t n = L.num_rows - r0 < chunk ? L.num_rows - r0 : chunk;

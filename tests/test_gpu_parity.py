@@ -478,11 +478,13 @@ def test_cu_masked_stream_gives_identical_results(num_cus):
 
 def test_row_count_beyond_one_dispatch():
     # 70 M rows of 8 bf16 elements run 64-thread workgroups: 4.5e9 work-items,
-    # more than one dispatch carries (below 2^31).  One workgroup per row
-    # then takes three dispatches over consecutive row ranges; the
-    # consecutive-rows kernel asked for 69 M workgroups (35 M of them holding
-    # two rows, 2.2e9 work-items) is capped to 33.5 M workgroups of three
-    # rows.  Every row must still be computed, once, with the same bits.
+    # more than one dispatch carries (below 2^31).  The fused launch, whose
+    # dispatches also stay within 768 MiB of traffic, takes seven dispatches
+    # of 10 M rows; the unfused kernels take three over consecutive row
+    # ranges; the consecutive-rows kernel asked for 69 M workgroups (35 M of
+    # them holding two rows, 2.2e9 work-items) is capped to 33.5 M workgroups
+    # of three rows.  Every row must still be computed, once, with the same
+    # bits, on both sides of every dispatch boundary.
     T, h, N = 70_000_000, 8, 2
     chunk = (2 ** 31 - 1) // 64
     g = torch.Generator(device="cuda")
@@ -504,6 +506,7 @@ def test_row_count_beyond_one_dispatch():
     rng = np.random.default_rng(11)
     idx = np.unique(np.concatenate([
         np.arange(4), np.arange(chunk - 3, chunk + 3), np.arange(2 * chunk - 3, 2 * chunk + 3),
+        *[np.arange(k * 10_000_000 - 3, k * 10_000_000 + 3) for k in range(1, 7)],
         np.arange(T - 4, T), rng.integers(0, T, 4000)]))
     ti = torch.from_numpy(idx).to("cuda")
     p_host = [to_host(parts[i].index_select(0, ti)) for i in range(N)]
