@@ -49,7 +49,8 @@ constexpr int kMaxCappedPartials = 8;
 //    best with D = 2 (23.2 against 23.9 us, 25.9 against 26.9); for N <= 4
 //    loading everything at once stays best (N = 2: 16.0 against 16.6 us).
 //  * 512 x 1 class (h = 4096, T = 8192): D = 1, N = 8 120.2 against 124.5 us;
-//    N = 2 53.3 against 54.0.
+//    N = 2 53.3 against 54.0.  Two in flight is slower at every N tried (N = 8:
+//    124.2 against 118.6 us; N = 16 at T = 4096: 111.0 against 104.1).
 //  * 512 x 4 class (h = 16384, T = 2048): 1024 x 2 loading one vector slot
 //    at a time, each in sequence with one tensor in flight (46 VGPRs, 8 waves
 //    per SIMD): N = 2 56.8 against 59.5 us, N = 4 77.8 against 79.7, N = 8
