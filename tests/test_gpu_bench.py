@@ -17,14 +17,16 @@ pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-@pytest.mark.parametrize("mode", ["full", "shard"])
-def test_bench_line_keeps_the_contract(mode):
+@pytest.mark.parametrize("mode,extra,rows", [
+    ("full", [], 1024), ("shard", [], 128),
+    ("full", ["--tokens", "300", "--partials", "3", "--no-split"], 300)])
+def test_bench_line_keeps_the_contract(mode, extra, rows):
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
-    print(f"[case] bench.py --mode {mode} --steps 40 --warmup 10", flush=True)
+    print(f"[case] bench.py --mode {mode} --steps 40 --warmup 10 {' '.join(extra)}", flush=True)
     run = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--mode", mode,
                           "--steps", "40", "--warmup", "10", "--cpu-seconds", "0.5",
-                          "--no-unfused"], capture_output=True, text=True, timeout=240)
+                          "--no-unfused", *extra], capture_output=True, text=True, timeout=240)
     assert run.returncode == 0, run.stderr[-2000:]
     lines = [ln for ln in run.stdout.splitlines() if ln.strip()]
     assert len(lines) == 1
@@ -36,8 +38,10 @@ def test_bench_line_keeps_the_contract(mode):
     assert d["unit"] == "GB/s" and d["n_gpus"] == 1 and d["steps"] == 40 and d["warmup"] == 10
     assert d["higher_is_better"] is True and d["vs_baseline"] is None
     cfg = d["config"]
-    rows = cfg["rows"]
-    assert rows == (1024 if mode == "full" else 128)
+    assert cfg["rows"] == rows
+    if extra:
+        assert cfg["num_tokens"] == 300 and cfg["num_partials"] == 3
+        assert d["roofline"]["traffic"] is None    # counters belong to the default shape only
     step_bytes = (cfg["num_partials"] + 3) * rows * cfg["hidden"] * 2
     assert abs(d["value"] - step_bytes / (d["ms_per_step"] * 1e-3) / 1e9) <= 0.01 * d["value"]
     r = d["roofline"]
