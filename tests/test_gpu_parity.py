@@ -519,6 +519,28 @@ def test_row_count_beyond_one_dispatch():
     check(to_host(rout_u.index_select(0, ti)), xu, "bf16", "unfused residual_out")
 
 
+def test_long_call_cut_into_dispatches():
+    # 8193 rows of h = 8192 with N = 8 move 1.48 GB, more than one dispatch
+    # may (768 MiB): the call runs as three dispatches of 2731 rows.  Rows on
+    # both sides of each boundary match the oracle, and every row matches the
+    # grid launch, whose dispatches are laid out differently.
+    T, h, N = 8193, 8192, 8
+    d = make_inputs("llama70b", num_tokens=T, hidden=h)
+    parts, res, w = upload(d)
+    say(f"fused, T={T} h={h} N={N}: three dispatches")
+    out, rout = tw.tw_fused_reduce_rmsnorm(parts, res, w, d["eps"])
+    say("grid launch over the same rows")
+    out_g, rout_g = tw.tw_fused_reduce_rmsnorm_grid(parts, res, w, d["eps"], 700)
+    torch.cuda.synchronize()
+    assert torch.equal(out_g, out) and torch.equal(rout_g, rout)
+    rows = np.unique(np.concatenate([np.arange(0, 3), np.arange(2729, 2734),
+                                     np.arange(5460, 5465), np.arange(T - 3, T)]))
+    y, x, _ = oracle.fused_reduce_rmsnorm([p[rows] for p in d["partials"]], d["residual"][rows],
+                                          d["weight"], d["eps"], "bf16")
+    check(to_host(out)[rows], y, "bf16", "out")
+    check(to_host(rout)[rows], x, "bf16", "residual_out")
+
+
 def test_binding_rejects_mismatched_tensors():
     d = make_inputs("llama70b", num_tokens=8, hidden=256)
     parts, res, w = upload(d)
