@@ -48,6 +48,9 @@ constexpr int kMaxCappedPartials = 8;
 //    50.3 against 55.3 (T = 4096, N = 8: 117.5 against 123.2).  N = 5, 6 do
 //    best with D = 2 (23.2 against 23.9 us, 25.9 against 26.9); for N <= 4
 //    loading everything at once stays best (N = 2: 16.0 against 16.6 us).
+//    Re-measured with the preloaded kernel arguments, D = 1 still wins from
+//    N = 7 on: N = 8 30.72 against 31.27 us (T = 4096: 117.8 against 124.8),
+//    N = 16 50.5 against 52.9.
 //  * 512 x 1 class (h = 4096, T = 8192): D = 1, N = 8 120.2 against 124.5 us;
 //    N = 2 53.3 against 54.0.  Two in flight is slower at every N tried (N = 8:
 //    124.2 against 118.6 us; N = 16 at T = 4096: 111.0 against 104.1).
