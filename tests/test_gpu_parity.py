@@ -541,6 +541,47 @@ def test_long_call_cut_into_dispatches():
     check(to_host(rout)[rows], x, "bf16", "residual_out")
 
 
+def test_random_shapes_match_oracle():
+    # Seeded random shapes across the supported range: N in 1..16, T in
+    # 1..70, row widths from one 16-byte vector to the largest row (around
+    # every geometry boundary), both dtypes, eps 1e-6 to 1e-2.  Every
+    # third case also runs shard k and a grid launch, which must give the
+    # same bits on their rows.
+    rng = np.random.default_rng(2024)
+    for case in range(60):
+        dtype = "bf16" if rng.random() < 0.6 else "f32"
+        per_vec = 8 if dtype == "bf16" else 4
+        max_vec = (65536 if dtype == "bf16" else 32768) // per_vec
+        nvec = int(rng.choice([1, 2, 3, 7, 31, 64, 127, 256, 511, 512, 513, 1023, 1024, 1025,
+                               2047, 2048, 2049, 4095, 4096, max_vec - 1, max_vec]))
+        h = nvec * per_vec
+        N = int(rng.integers(1, 17))
+        T = int(rng.integers(1, 71)) if h <= 16384 else int(rng.integers(1, 9))
+        eps = float(rng.choice([1e-6, 1e-5, 1e-2]))
+        wl = WORKLOADS["llama70b"] if dtype == "bf16" else WORKLOADS["tiny"]
+        d = make_inputs(wl, num_tokens=T, hidden=h, seed=1000 + case)
+        d["partials"] = np.concatenate([d["partials"]] * (N // len(d["partials"]) + 1))[:N]
+        d["eps"] = eps
+        say(f"random case {case}: N={N} T={T} h={h} {dtype} eps={eps}")
+        parts, res, w = upload(d)
+        out, rout = _run_full(parts, res, w, eps)
+        y, x, _ = _oracle(d)
+        check(out, y, dtype, f"case {case} out")
+        check(rout, x, dtype, f"case {case} residual_out")
+        if case % 3 == 0:
+            k = int(rng.integers(0, N))
+            lo, hi = oracle.shard_rows(T, N, k).start, oracle.shard_rows(T, N, k).stop
+            o_s, r_s = torch.zeros_like(res), torch.zeros_like(res)
+            tw.tw_shard_rmsnorm(parts, res, w, eps, k, out=o_s, residual_out=r_s)
+            o_g, r_g = tw.tw_fused_reduce_rmsnorm_grid(parts, res, w, eps,
+                                                       int(rng.integers(1, T + 1)))
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(to_host(o_s)[lo:hi], out[lo:hi])
+            np.testing.assert_array_equal(to_host(r_s)[lo:hi], rout[lo:hi])
+            np.testing.assert_array_equal(to_host(o_g), out)
+            np.testing.assert_array_equal(to_host(r_g), rout)
+
+
 def test_binding_rejects_mismatched_tensors():
     d = make_inputs("llama70b", num_tokens=8, hidden=256)
     parts, res, w = upload(d)
