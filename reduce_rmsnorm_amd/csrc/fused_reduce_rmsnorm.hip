@@ -26,9 +26,12 @@
 //    table (geometry.h) says which row classes and partial counts use the
 //    sequenced order; a launch too small to fill the CUs issues all loads at
 //    once regardless, since it would otherwise wait out one latency per
-//    tensor.  Out of range vectors (h not a multiple of BLOCK*VPT*elems) load
-//    a clamped, valid address and contribute zero, so no branch splits a load
-//    batch.
+//    tensor.  In the sequenced order a wave pauses briefly (s_sleep, a pace
+//    set per row class and N in geometry.h) after adding each tensor, before
+//    requesting the next: with many tensors per row, fewer requests in flight
+//    stream faster.  Out of range vectors (h not a multiple of
+//    BLOCK*VPT*elems) load a clamped, valid address and contribute zero, so no
+//    branch splits a load batch.
 //  * The partials and the residual are summed with an error-free
 //    transformation (TwoSum) into a float32 pair (s, c); x = s + c.  For bf16
 //    the stored residual is rounded to odd in float32 first and then to bf16
@@ -113,9 +116,10 @@ _Pragma("unroll")                                                               
 //    CHUNK == VPT every load of the row is in flight before the first use;
 //    wide rows take CHUNK slots at a time so their values fit in registers.
 //  * SEQ == D > 0: the tensors are loaded in summation order, D of them in
-//    flight: tensor i + D is requested once tensor i has been added.  Fewer
-//    DRAM regions are open at a time across the chip, which streams faster
-//    when there are many partials.  The first loads go out before anything
+//    flight: tensor i + D is requested once tensor i has been added (and,
+//    with PACE > 0, after a pause of PACE * 64 clocks).  Fewer DRAM regions
+//    are open at a time across the chip, which streams faster when there are
+//    many partials.  The first loads go out before anything
 //    else; the other tensors' addresses and the weight row are fetched while
 //    they are in flight (scheduling barriers keep that order).
 #define TW_FUSED_ROW_BODY(ROW_EXPR)                                                    \
@@ -180,6 +184,7 @@ _Pragma("unroll")                                                               
           }                                                                            \
         }                                                                              \
         __builtin_amdgcn_sched_barrier(0);                                             \
+        if constexpr (PACE > 0) __builtin_amdgcn_s_sleep(PACE);                        \
         if (i + SEQ <= N) {                                                            \
 _Pragma("unroll")                                                                      \
           for (int jj = 0; jj < CHUNK; ++jj)                                           \
@@ -247,7 +252,7 @@ _Pragma("unroll")                                                               
 // One workgroup per row: the launch grid is the row count.  k_first,
 // k_row_begin and k_nvec repeat a.partials[0], a.row_begin and a.nvec as
 // preloaded scalar arguments.
-template <int N, int BLOCK, int VPT, bool BF16, int WPE, int CHUNK, int SEQ>
+template <int N, int BLOCK, int VPT, bool BF16, int WPE, int CHUNK, int SEQ, int PACE>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(WPE)))
 void fused_reduce_rmsnorm_kernel(const u32x4* k_first, int64_t k_row_begin, int32_t k_nvec,
                                  KArgs a) {
@@ -263,7 +268,7 @@ void fused_reduce_rmsnorm_kernel(const u32x4* k_first, int64_t k_row_begin, int3
 // A barrier between rows keeps a row's wave partial sums from overwriting the
 // previous row's while a slower wave still reads them.  Few workgroups are
 // launched by design, so no occupancy cap is requested.
-template <int N, int BLOCK, int VPT, bool BF16, int CHUNK, int SEQ>
+template <int N, int BLOCK, int VPT, bool BF16, int CHUNK, int SEQ, int PACE>
 __global__ __launch_bounds__(BLOCK) void fused_reduce_rmsnorm_rows_kernel(KArgs a,
                                                                           int64_t rows_per_wg,
                                                                           int64_t row_end) {
@@ -289,20 +294,25 @@ using RowsKernelFn = void (*)(KArgs, int64_t, int64_t);
 constexpr int load_order(int g, int n, bool seq_order) {
   return seq_order ? fused_geometry(g, n).seq : 0;
 }
+constexpr int load_pace(int g, int n, bool seq_order) {
+  return load_order(g, n, seq_order) > 0 ? fused_pace(g, n) : 0;
+}
 template <bool BF16, bool SEQ_ORDER, int G, int... Ns>
 constexpr std::array<KernelFn, sizeof...(Ns)> row_of(std::integer_sequence<int, Ns...>) {
   return {&fused_reduce_rmsnorm_kernel<Ns + 1, fused_geometry(G, Ns + 1).block,
                                        fused_geometry(G, Ns + 1).vpt, BF16,
                                        fused_geometry(G, Ns + 1).waves_per_eu,
                                        fused_geometry(G, Ns + 1).chunk,
-                                       load_order(G, Ns + 1, SEQ_ORDER)>...};
+                                       load_order(G, Ns + 1, SEQ_ORDER),
+                                       load_pace(G, Ns + 1, SEQ_ORDER)>...};
 }
 template <bool BF16, bool SEQ_ORDER, int G, int... Ns>
 constexpr std::array<RowsKernelFn, sizeof...(Ns)> rows_row_of(std::integer_sequence<int, Ns...>) {
   return {&fused_reduce_rmsnorm_rows_kernel<Ns + 1, fused_geometry(G, Ns + 1).block,
                                             fused_geometry(G, Ns + 1).vpt, BF16,
                                             fused_geometry(G, Ns + 1).chunk,
-                                            load_order(G, Ns + 1, SEQ_ORDER)>...};
+                                            load_order(G, Ns + 1, SEQ_ORDER),
+                                            load_pace(G, Ns + 1, SEQ_ORDER)>...};
 }
 
 template <bool BF16, bool SEQ_ORDER, int... Gs>

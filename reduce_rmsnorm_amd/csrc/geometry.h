@@ -80,6 +80,31 @@ constexpr Geometry fused_geometry(int g, int n) {
 constexpr int kNumCUs = 256;
 constexpr int64_t seq_min_workgroups(int block) { return (int64_t)kNumCUs * (8 * 4 * 64 / block); }
 
+// Pacing of the sequenced load order: after adding a tensor, a wave pauses
+// for PACE * 64 clocks (s_sleep) before it requests the next one.  Fewer
+// requests in flight across the chip let HBM work more efficiently, and the
+// more tensors a row has, the more that pays.  Measured on MI355X (bf16,
+// rotated past the MALL, times per launch; PACE 0 / best):
+//  * 1024 x 1 class (h = 8192, T = 1024): N = 5, 6 best unpaced; N = 8 30.83
+//    against 30.73 us (PACE 4), N = 12 40.60 against 40.18 (8), N = 16 50.81
+//    against 49.56 (10).
+//  * 512 x 1 class (h = 4096, T = 4096): N <= 6 best unpaced (N = 2: 28.27
+//    against 28.35 at PACE 2); N = 8 60.26 against 59.56 (8), N = 12 82.93
+//    against 78.42 (10), N = 16 106.10 against 96.67 (12).
+//  * 1024 x 2 class (h = 16384, T = 1024): N <= 4 best unpaced; N = 8 61.23
+//    against 60.04 (10), N = 16 103.48 against 97.44 (12).
+// Partial counts between the measured ones take the nearer measured pace.
+constexpr int fused_pace(int g, int n) {
+  const Geometry k = kGeometry[g];
+  if (k.block == 512 && k.vpt == 2 && n >= 7)           // 1024 x 1, sequenced
+    return n <= 8 ? 4 : n <= 10 ? 5 : n <= 12 ? 8 : 10;
+  if (k.block == 512 && k.vpt == 1 && n >= 8)           // 512 x 1, sequenced
+    return n <= 8 ? 8 : n <= 12 ? 10 : 12;
+  if (k.block == 512 && k.vpt == 4 && n >= 6)           // 1024 x 2, sequenced
+    return n <= 6 ? 4 : n <= 12 ? 10 : 12;
+  return 0;
+}
+
 constexpr int kNumGeometries = sizeof(kGeometry) / sizeof(kGeometry[0]);
 constexpr int kMaxVectors = 8192;
 

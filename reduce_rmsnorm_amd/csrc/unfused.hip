@@ -52,15 +52,16 @@ struct AddNormArgs {
   float eps;
 };
 
-// The reduce step uses the fused kernel's row geometry and load orders (all
-// loads of CHUNK slots at once, or the partials in summation order with SEQ in
-// flight), so that the comparator streams as well as the fused kernel does.
+// The reduce step uses the fused kernel's row geometry, load orders and
+// pacing (all loads of CHUNK slots at once, or the partials in summation order
+// with SEQ in flight and a PACE pause between them), so that the comparator
+// streams as well as the fused kernel does.
 // Like the fused kernel it takes partial 0's address and the row length as
 // leading scalar arguments (k_first, k_nvec: copies of a.partials[0] and
 // a.nvec) that this file's build preloads into SGPRs, so a wave's first load
 // does not wait for the argument block.  No value is shared between threads,
 // so the geometry never changes a bit.
-template <int N, int BLOCK, int VPT, bool BF16, int WPE, int CHUNK, int SEQ>
+template <int N, int BLOCK, int VPT, bool BF16, int WPE, int CHUNK, int SEQ, int PACE>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(WPE)))
 void reduce_kernel(const u32x4* k_first, int32_t k_nvec, ReduceArgs a) {
   constexpr int E = Elem<BF16>::kPerVec;
@@ -121,6 +122,7 @@ void reduce_kernel(const u32x4* k_first, int32_t k_nvec, ReduceArgs a) {
       }
       if constexpr (SEQ > 0) {
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PACE > 0) __builtin_amdgcn_s_sleep(PACE);
         if (i + SEQ < N) {
 #pragma unroll
           for (int jj = 0; jj < CHUNK; ++jj)
@@ -211,6 +213,9 @@ using AddNormFn = void (*)(AddNormArgs);
 constexpr int reduce_order(int g, int n, bool seq_order) {
   return seq_order ? fused_geometry(g, n).seq : 0;
 }
+constexpr int reduce_pace(int g, int n, bool seq_order) {
+  return reduce_order(g, n, seq_order) > 0 ? fused_pace(g, n) : 0;
+}
 // Occupancy cap of the reduce step: the fused geometry's, except above ten
 // partials, where the cap would make the compiler spill the loaded values.
 constexpr int reduce_waves(int g, int n) { return n <= 10 ? fused_geometry(g, n).waves_per_eu : 1; }
@@ -218,7 +223,8 @@ template <bool BF16, bool SEQ_ORDER, int G, int... Ns>
 constexpr std::array<ReduceFn, sizeof...(Ns)> reduce_row(std::integer_sequence<int, Ns...>) {
   return {&reduce_kernel<Ns + 1, fused_geometry(G, Ns + 1).block, fused_geometry(G, Ns + 1).vpt,
                          BF16, reduce_waves(G, Ns + 1),
-                         fused_geometry(G, Ns + 1).chunk, reduce_order(G, Ns + 1, SEQ_ORDER)>...};
+                         fused_geometry(G, Ns + 1).chunk, reduce_order(G, Ns + 1, SEQ_ORDER),
+                         reduce_pace(G, Ns + 1, SEQ_ORDER)>...};
 }
 template <bool BF16, bool SEQ_ORDER, int... Gs>
 constexpr std::array<std::array<ReduceFn, kMaxPartials>, sizeof...(Gs)> reduce_table(
