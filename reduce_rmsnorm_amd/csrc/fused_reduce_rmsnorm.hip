@@ -77,6 +77,7 @@ struct KArgs {
   u32x4* out;
   u32x4* residual_out;
   int64_t row_begin;
+  int64_t row_end;   // one past the launch's last row (read by the strided kernel)
   int32_t nvec;      // 16-byte vectors per row
   float hidden;      // h as float32 (exact: h <= 2^24)
   float eps;
@@ -102,6 +103,60 @@ _Pragma("unroll")                                                               
       __builtin_nontemporal_store(pack<BF16>(keep), a.residual_out + base + vi[J]);    \
 _Pragma("unroll")                                                                      \
     for (int e = 0; e < E; ++e) ss = __builtin_fmaf(x[J][e], x[J][e], ss);             \
+  }
+
+// The sequenced summation of CHUNK vector slots starting at slot J0 of the
+// row at `base`: tensor i is added into (s, c) once it has arrived, then,
+// after a pause of PACE * 64 clocks, tensor i + SEQ is requested.  Tensors
+// 0 .. SEQ-1 must already be in flight in raw[], and tp[] must hold the
+// tensors' addresses.
+#define TW_SEQ_ADD(J0)                                                                 \
+_Pragma("unroll")                                                                      \
+  for (int i = 0; i <= N; ++i) {                                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+_Pragma("unroll")                                                                      \
+    for (int jj = 0; jj < CHUNK; ++jj) {                                               \
+      if (i == 0) {                                                                    \
+        unpack<BF16>(raw[0][jj], s[jj]);                                               \
+_Pragma("unroll")                                                                      \
+        for (int e = 0; e < E; ++e) c[jj][e] = 0.0f;                                   \
+      } else {                                                                         \
+        float t[E];                                                                    \
+        unpack<BF16>(raw[i][jj], t);                                                   \
+_Pragma("unroll")                                                                      \
+        for (int e = 0; e < E; ++e) two_sum_into(s[jj][e], c[jj][e], t[e]);            \
+      }                                                                                \
+    }                                                                                  \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+    if constexpr (PACE > 0) __builtin_amdgcn_s_sleep(PACE);                            \
+    if (i + SEQ <= N) {                                                                \
+_Pragma("unroll")                                                                      \
+      for (int jj = 0; jj < CHUNK; ++jj)                                               \
+        raw[i + SEQ <= N ? i + SEQ : N][jj] =                                          \
+            __builtin_nontemporal_load(tp[i + SEQ <= N ? i + SEQ : N] + base +          \
+                                       vi[(J0) + jj]);                                 \
+    }                                                                                  \
+  }
+
+// The end of a row: the row's sum of squares (wave, then the waves in order
+// through the LDS array PART[BLOCK / 64]), rs, and the `out` stores.
+#define TW_NORMALIZE(PART)                                                             \
+  /* Row sum of squares: wave, then waves in order through LDS. */                     \
+  const float wsum = wave_sum(ss);                                                     \
+  if ((tid & 63) == 0) (PART)[tid >> 6] = wsum;                                        \
+  __syncthreads();                                                                     \
+  float total = (PART)[0];                                                             \
+_Pragma("unroll")                                                                      \
+  for (int w = 1; w < NW; ++w) total += (PART)[w];                                     \
+  const float rs = __builtin_amdgcn_rsqf(total / a.hidden + a.eps);                    \
+                                                                                       \
+_Pragma("unroll")                                                                      \
+  for (int j = 0; j < VPT; ++j) {                                                      \
+    float w[E], y[E];                                                                  \
+    unpack<BF16>(wraw[j], w);                                                          \
+_Pragma("unroll")                                                                      \
+    for (int e = 0; e < E; ++e) y[e] = (x[j][e] * rs) * w[e];                          \
+    if (valid[j]) __builtin_nontemporal_store(pack<BF16>(y), a.out + base + vi[j]);    \
   }
 
 // The per-row body of both fused kernels: everything the fused step does to
@@ -167,32 +222,7 @@ _Pragma("unroll")                                                               
         }                                                                              \
       }                                                                                \
       __builtin_amdgcn_sched_barrier(0);                                               \
-_Pragma("unroll")                                                                      \
-      for (int i = 0; i <= N; ++i) {                                                   \
-        __builtin_amdgcn_sched_barrier(0);                                             \
-_Pragma("unroll")                                                                      \
-        for (int jj = 0; jj < CHUNK; ++jj) {                                           \
-          if (i == 0) {                                                                \
-            unpack<BF16>(raw[0][jj], s[jj]);                                           \
-_Pragma("unroll")                                                                      \
-            for (int e = 0; e < E; ++e) c[jj][e] = 0.0f;                               \
-          } else {                                                                     \
-            float t[E];                                                                \
-            unpack<BF16>(raw[i][jj], t);                                               \
-_Pragma("unroll")                                                                      \
-            for (int e = 0; e < E; ++e) two_sum_into(s[jj][e], c[jj][e], t[e]);        \
-          }                                                                            \
-        }                                                                              \
-        __builtin_amdgcn_sched_barrier(0);                                             \
-        if constexpr (PACE > 0) __builtin_amdgcn_s_sleep(PACE);                        \
-        if (i + SEQ <= N) {                                                            \
-_Pragma("unroll")                                                                      \
-          for (int jj = 0; jj < CHUNK; ++jj)                                           \
-            raw[i + SEQ <= N ? i + SEQ : N][jj] =                                      \
-                __builtin_nontemporal_load(tp[i + SEQ <= N ? i + SEQ : N] + base +      \
-                                           vi[j0 + jj]);                               \
-        }                                                                              \
-      }                                                                                \
+      TW_SEQ_ADD(j0)                                                                   \
 _Pragma("unroll")                                                                      \
       for (int jj = 0; jj < CHUNK; ++jj) TW_FINISH_SLOT(j0 + jj, s[jj], c[jj])         \
     }                                                                                  \
@@ -231,23 +261,7 @@ _Pragma("unroll")                                                               
     for (int j = 0; j < VPT; ++j) wraw[j] = a.weight[vi[j]];                           \
   }                                                                                    \
                                                                                        \
-  /* Row sum of squares: wave, then waves in order through LDS. */                     \
-  const float wsum = wave_sum(ss);                                                     \
-  if ((tid & 63) == 0) wave_part[tid >> 6] = wsum;                                     \
-  __syncthreads();                                                                     \
-  float total = wave_part[0];                                                          \
-_Pragma("unroll")                                                                      \
-  for (int w = 1; w < NW; ++w) total += wave_part[w];                                  \
-  const float rs = __builtin_amdgcn_rsqf(total / a.hidden + a.eps);                    \
-                                                                                       \
-_Pragma("unroll")                                                                      \
-  for (int j = 0; j < VPT; ++j) {                                                      \
-    float w[E], y[E];                                                                  \
-    unpack<BF16>(wraw[j], w);                                                          \
-_Pragma("unroll")                                                                      \
-    for (int e = 0; e < E; ++e) y[e] = (x[j][e] * rs) * w[e];                          \
-    if (valid[j]) __builtin_nontemporal_store(pack<BF16>(y), a.out + base + vi[j]);    \
-  }
+  TW_NORMALIZE(wave_part)
 
 // One workgroup per row: the launch grid is the row count.  k_first,
 // k_row_begin and k_nvec repeat a.partials[0], a.row_begin and a.nvec as
@@ -260,6 +274,79 @@ void fused_reduce_rmsnorm_kernel(const u32x4* k_first, int64_t k_row_begin, int3
   constexpr int NW = BLOCK / 64;
   __shared__ float wave_part[NW];
   TW_FUSED_ROW_BODY(k_row_begin + blockIdx.x)
+}
+
+// One resident round of workgroups over a launch of one to four rounds of
+// rows: workgroup b takes rows b, b + G, b + 2G, ... (G, the grid, is one
+// round), in the sequenced load order.  Before a row's sum of squares is
+// reduced, the workgroup requests the first tensors of its next row, so the
+// barrier and the `out` stores overlap that row's first loads.  With one
+// workgroup per row, the rows past the last full round start on whichever
+// CUs free up first; here the workgroups that carry them were placed with
+// the first round.  Measured, that is faster when the last round is at most
+// half full (the launch rule and its figures are in geometry.h).  The per-row
+// arithmetic is the one-row kernel's (the same macros), so a row gives the
+// same bits in either kernel.  Two LDS buffers for the wave sums, used alternately,
+// make one barrier per row enough: a wave can only write a buffer again after
+// passing the next row's barrier, which every wave reaches after reading it.
+template <int N, int BLOCK, int VPT, bool BF16, int WPE, int CHUNK, int SEQ, int PACE>
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(WPE)))
+void fused_reduce_rmsnorm_strided_kernel(const u32x4* k_first, int64_t k_row_begin,
+                                         int32_t k_nvec, KArgs a) {
+  static_assert(SEQ > 0 && CHUNK == VPT, "the strided kernel loads all slots in one sequence");
+  constexpr int E = Elem<BF16>::kPerVec;
+  constexpr int NW = BLOCK / 64;
+  __shared__ float wave_part[2][NW];
+  const int tid = threadIdx.x;
+  const int nvec = k_nvec;
+  int vi[VPT];
+  bool valid[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int v = tid + j * BLOCK;
+    valid[j] = v < nvec;
+    vi[j] = valid[j] ? v : nvec - 1;
+  }
+  int64_t row = k_row_begin + blockIdx.x;
+  u32x4 raw[N + 1][CHUNK];
+#pragma unroll
+  for (int i = 0; i < SEQ && i <= N; ++i)
+#pragma unroll
+    for (int jj = 0; jj < CHUNK; ++jj)
+      raw[i][jj] = __builtin_nontemporal_load(TW_TENSOR(i) + row * (int64_t)nvec + vi[jj]);
+  __builtin_amdgcn_sched_barrier(0);
+  const u32x4* tp[N + 1];
+#pragma unroll
+  for (int i = 0; i <= N; ++i) tp[i] = TW_TENSOR(i);
+  u32x4 wraw[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) wraw[j] = a.weight[vi[j]];
+  __builtin_amdgcn_sched_barrier(0);
+  for (int parity = 0;; parity ^= 1) {
+    // Recomputed from the row each time: carried across iterations, the
+    // compiler keeps it in vector registers and spills.
+    const int64_t base = row * (int64_t)nvec;
+    float x[VPT][E];
+    float ss = 0.0f;
+    float s[CHUNK][E], c[CHUNK][E];
+    TW_SEQ_ADD(0)
+#pragma unroll
+    for (int jj = 0; jj < CHUNK; ++jj) TW_FINISH_SLOT(jj, s[jj], c[jj])
+    const int64_t next = row + gridDim.x;
+    const bool more = next < a.row_end;           // the same for the whole workgroup
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < SEQ && i <= N; ++i)
+#pragma unroll
+        for (int jj = 0; jj < CHUNK; ++jj)
+          raw[i][jj] = __builtin_nontemporal_load(tp[i] + next * (int64_t)nvec + vi[jj]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    TW_NORMALIZE(wave_part[parity])
+    if (!more) break;
+    row = next;
+  }
 }
 
 // A fixed number of workgroups: workgroup b takes the consecutive rows
@@ -306,6 +393,29 @@ constexpr std::array<KernelFn, sizeof...(Ns)> row_of(std::integer_sequence<int, 
                                        load_order(G, Ns + 1, SEQ_ORDER),
                                        load_pace(G, Ns + 1, SEQ_ORDER)>...};
 }
+// The strided kernel exists for the sequenced geometries that load all of a
+// thread's vector slots in one sequence (1024 x 1 and 512 x 1; the 1024 x 2
+// class, one slot at a time, would spill).
+template <bool BF16, int G, int NN>
+constexpr KernelFn strided_fn() {
+  if constexpr (fused_geometry(G, NN).seq > 0 &&
+                fused_geometry(G, NN).chunk == fused_geometry(G, NN).vpt)
+    return &fused_reduce_rmsnorm_strided_kernel<
+        NN, fused_geometry(G, NN).block, fused_geometry(G, NN).vpt, BF16,
+        fused_geometry(G, NN).waves_per_eu, fused_geometry(G, NN).chunk,
+        fused_geometry(G, NN).seq, fused_pace(G, NN)>;
+  else
+    return nullptr;
+}
+template <bool BF16, int G, int... Ns>
+constexpr std::array<KernelFn, sizeof...(Ns)> strided_row_of(std::integer_sequence<int, Ns...>) {
+  return {strided_fn<BF16, G, Ns + 1>()...};
+}
+template <bool BF16, int... Gs>
+constexpr std::array<std::array<KernelFn, kMaxPartials>, sizeof...(Gs)> strided_table_of(
+    std::integer_sequence<int, Gs...>) {
+  return {strided_row_of<BF16, Gs>(std::make_integer_sequence<int, kMaxPartials>{})...};
+}
 template <bool BF16, bool SEQ_ORDER, int G, int... Ns>
 constexpr std::array<RowsKernelFn, sizeof...(Ns)> rows_row_of(std::integer_sequence<int, Ns...>) {
   return {&fused_reduce_rmsnorm_rows_kernel<Ns + 1, fused_geometry(G, Ns + 1).block,
@@ -331,6 +441,9 @@ using Geoms = std::make_integer_sequence<int, kNumGeometries>;
 const std::array<std::array<std::array<std::array<KernelFn, kMaxPartials>, kNumGeometries>, 2>, 2>
     kTable = {{{table_of<false, false>(Geoms{}), table_of<false, true>(Geoms{})},
                {table_of<true, false>(Geoms{}), table_of<true, true>(Geoms{})}}};
+// [bf16]
+const std::array<std::array<std::array<KernelFn, kMaxPartials>, kNumGeometries>, 2> kStridedTable = {
+    {strided_table_of<false>(Geoms{}), strided_table_of<true>(Geoms{})}};
 const std::array<std::array<std::array<std::array<RowsKernelFn, kMaxPartials>, kNumGeometries>, 2>, 2>
     kRowsTable = {{{rows_table_of<false, false>(Geoms{}), rows_table_of<false, true>(Geoms{})},
                    {rows_table_of<true, false>(Geoms{}), rows_table_of<true, true>(Geoms{})}}};
@@ -370,8 +483,9 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
   const int block = geo.block;
   hipError_t e;
   if (L.max_workgroups <= 0 || L.max_workgroups >= L.num_rows) {
-    const bool seq = L.num_rows >= seq_min_workgroups(block);
-    const KernelFn fn = kTable[bf16][seq][g][L.num_partials - 1];
+    const int64_t round = seq_min_workgroups(block);
+    const bool seq = L.num_rows >= round;
+    const KernelFn strided_fn = kStridedTable[bf16][g][L.num_partials - 1];
     // Dispatches over consecutive row ranges of about equal size, each within
     // the byte and work-item limits; the per-row code is the same in each.
     const int64_t row_bytes = (int64_t)(L.num_partials + 3) * nvec * 16;
@@ -382,12 +496,16 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
     for (int64_t r0 = 0; r0 < L.num_rows && e == hipSuccess; r0 += chunk) {
       const int64_t n = L.num_rows - r0 < chunk ? L.num_rows - r0 : chunk;
       k.row_begin = L.row_begin + r0;
+      k.row_end = k.row_begin + n;
+      const bool strided = seq && strided_fn != nullptr && use_strided_grid(n, round);
+      const KernelFn fn = strided ? strided_fn : kTable[bf16][seq][g][L.num_partials - 1];
+      const int64_t grid = strided ? round : n;
       const u32x4* first = k.partials[0];
       int64_t row_begin = k.row_begin;
       int32_t nvec32 = k.nvec;
       void* args[] = {&first, &row_begin, &nvec32, &k};
-      e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)n), dim3(block), args,
-                          0, static_cast<hipStream_t>(L.stream));
+      e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid), dim3(block),
+                          args, 0, static_cast<hipStream_t>(L.stream));
     }
   } else {
     const int64_t cap = max_rows_per_dispatch(block);

@@ -80,6 +80,30 @@ constexpr Geometry fused_geometry(int g, int n) {
 constexpr int kNumCUs = 256;
 constexpr int64_t seq_min_workgroups(int block) { return (int64_t)kNumCUs * (8 * 4 * 64 / block); }
 
+// A sequenced launch whose rows are not a whole number of rounds leaves its
+// last round partly empty.  With one workgroup per row those last rows land
+// on whichever CUs free up first; launching one round of workgroups that each
+// take every round-th row (the strided kernel) keeps one or two extra rows
+// per CU instead, and overlaps each workgroup's row boundary with its next
+// row's first loads.  It wins while the last round is at most half full and
+// the launch is under four rounds; with fuller last rounds, and on whole or
+// longer launches, the hardware's own dispatch of one-row workgroups
+// balances better.  Measured on MI355X (N = 8 bf16, rotated past the MALL,
+// one-row kernel against strided, us per launch):
+//  * h = 8192, round 512: T = 520 22.47 / 22.10, 576 22.87 / 22.40, 640
+//    22.87 / 22.26, 768 25.29 / 24.41 (N = 16: 43.18 / 41.78), 1152
+//    36.91 / 36.16, 1280 38.96 / 38.06, 1792 52.77 / 52.02; not taken:
+//    896 28.09 / 28.25, 960 29.33 / 29.46, 1024 30.65 / 30.63, 1536
+//    44.91 / 45.36, 2048 59.04 / 59.55, 4096 117.1 / 120.6.
+//  * h = 4096, round 1024: T = 1280 23.31 / 22.71, 1536 25.28 / 24.99, 2560
+//    39.01 / 38.87; not taken: 1792 27.98 / 28.07, 3072 44.85 / 45.29, 4096
+//    59.32 / 60.09, 8192 116.6 / 121.6.
+// Both kernels do the same per-row arithmetic: the choice never changes a bit.
+constexpr bool use_strided_grid(int64_t rows, int64_t round) {
+  const int64_t tail = rows % round;
+  return rows > round && rows < 4 * round && tail > 0 && 2 * tail <= round;
+}
+
 // Pacing of the sequenced load order: after adding a tensor, a wave pauses
 // for PACE * 64 clocks (s_sleep) before it requests the next one.  Fewer
 // requests in flight across the chip let HBM work more efficiently, and the

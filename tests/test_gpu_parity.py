@@ -641,7 +641,9 @@ def test_load_order_never_changes_a_bit(h, N, dtype):
     # arithmetic is the same, so every row must come out bit-identical, and
     # both must meet the oracle.
     # Above one full round of workgroups at every width here (512 rows for the
-    # 1024-thread classes, 1024 rows for 512 x 1); the ragged widths (8184,
+    # 1024-thread classes, 1024 rows for 512 x 1), with a last round at most
+    # half full, so the full launch takes the strided kernel where the width
+    # has one (not h = 16384 or 12296 bf16, nor 8192 f32); the ragged widths (8184,
     # 12296, 3080) leave lanes that clamp their address inside the sequence.
     T = 1100
     d = make_inputs("llama70b" if dtype == "bf16" else "tiny", num_tokens=T, hidden=h, seed=40 + N)
@@ -661,6 +663,45 @@ def test_load_order_never_changes_a_bit(h, N, dtype):
     y, x, _ = _oracle(d, rows=rows)
     check(out[rows], y, dtype, "out")
     check(rout[rows], x, dtype, "residual_out")
+
+
+# Launches of one to four rounds of rows whose last round is at most half full
+# run one round of workgroups that each take every round-th row (one round:
+# 512 workgroups for the 1024-thread class, h = 8192 bf16 or 4096 f32; 1024
+# for the 512 x 1 class, h = 4096 bf16).  (h, N, dtype, T) below fall in that
+# window; N = 5 loads two tensors ahead, the others one; 8184 and 4088 leave
+# lanes that clamp their address.
+STRIDED = [(8192, 8, "bf16", 768), (8192, 5, "bf16", 600), (8192, 16, "bf16", 1280),
+           (8184, 7, "bf16", 700), (4096, 8, "bf16", 1280), (4096, 2, "bf16", 1536),
+           (4088, 3, "bf16", 1100), (4096, 8, "f32", 640), (4096, 12, "f32", 1700)]
+
+
+@pytest.mark.parametrize("h,N,dtype,T", STRIDED)
+def test_strided_launch_matches_one_row_launches_and_oracle(h, N, dtype, T):
+    d = make_inputs("llama70b" if dtype == "bf16" else "tiny", num_tokens=T, hidden=h, seed=70 + N)
+    d["partials"] = np.concatenate([d["partials"]] + [d["partials"][:, ::-1]] * 8)[:N]
+    parts, res, w = upload(d)
+    round_rows = 1024 if (h * (2 if dtype == "bf16" else 4)) <= 8192 else 512
+    whole = (T // round_rows) * round_rows
+    say(f"strided: T={T} h={h} N={N} {dtype}; pieces [0,{whole}) and [{whole},{T})")
+    out = torch.full_like(res, float("nan"))
+    rout = torch.full_like(res, float("nan"))
+    tw.tw_fused_reduce_rmsnorm(parts, res, w, d["eps"], out=out, residual_out=rout)
+    # The same rows as whole rounds of one-row workgroups plus the remainder,
+    # which is too small for the sequenced order and issues all loads at once.
+    out_p = torch.full_like(res, float("nan"))
+    rout_p = torch.full_like(res, float("nan"))
+    for lo, hi in ((0, whole), (whole, T)):
+        tw.tw_fused_reduce_rmsnorm(parts[:, lo:hi], res[lo:hi], w, d["eps"], out=out_p[lo:hi],
+                                   residual_out=rout_p[lo:hi])
+    torch.cuda.synchronize()
+    o, ro = to_host(out), to_host(rout)
+    np.testing.assert_array_equal(to_host(out_p), o)
+    np.testing.assert_array_equal(to_host(rout_p), ro)
+    rows = sorted(set(range(0, T, 23)) | {T - 1, whole - 1, whole})
+    y, x, _ = _oracle(d, rows=rows)
+    check(o[rows], y, dtype, "out")
+    check(ro[rows], x, dtype, "residual_out")
 
 
 @pytest.mark.parametrize("eps", [0.0, 1e-12, 1e-5, 1.0])
