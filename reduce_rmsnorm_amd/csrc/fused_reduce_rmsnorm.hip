@@ -484,7 +484,7 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
   hipError_t e;
   if (L.max_workgroups <= 0 || L.max_workgroups >= L.num_rows) {
     const int64_t round = seq_min_workgroups(block);
-    const bool seq = L.num_rows >= round;
+    const bool seq = use_sequenced_order(L.num_rows, round, L.num_partials, geo.seq);
     const KernelFn strided_fn = kStridedTable[bf16][g][L.num_partials - 1];
     // Dispatches over consecutive row ranges of about equal size, each within
     // the byte and work-item limits; the per-row code is the same in each.

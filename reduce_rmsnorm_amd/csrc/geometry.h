@@ -83,13 +83,14 @@ constexpr int64_t seq_min_workgroups(int block) { return (int64_t)kNumCUs * (8 *
 // A sequenced launch whose rows are not a whole number of rounds leaves its
 // last round partly empty.  With one workgroup per row those last rows land
 // on whichever CUs free up first; launching one round of workgroups that each
-// take every round-th row (the strided kernel) keeps one or two extra rows
-// per CU instead, and overlaps each workgroup's row boundary with its next
-// row's first loads.  It wins while the last round is at most half full and
+// take every round-th row (the strided kernel) places the workgroups that
+// carry them with the first round instead, and overlaps each workgroup's row
+// boundary with its next row's first loads.  It wins while the last round is at most half full and
 // the launch is under four rounds; with fuller last rounds, and on whole or
 // longer launches, the hardware's own dispatch of one-row workgroups
 // balances better.  Measured on MI355X (N = 8 bf16, rotated past the MALL,
-// one-row kernel against strided, us per launch):
+// one-row kernel against strided, us per launch; at N = 8, launches below one
+// and a half rounds issue all loads at once instead, see use_sequenced_order):
 //  * h = 8192, round 512: T = 520 22.47 / 22.10, 576 22.87 / 22.40, 640
 //    22.87 / 22.26, 768 25.29 / 24.41 (N = 16: 43.18 / 41.78), 1152
 //    36.91 / 36.16, 1280 38.96 / 38.06, 1792 52.77 / 52.02; not taken:
@@ -102,6 +103,39 @@ constexpr int64_t seq_min_workgroups(int block) { return (int64_t)kNumCUs * (8 *
 constexpr bool use_strided_grid(int64_t rows, int64_t round) {
   const int64_t tail = rows % round;
   return rows > round && rows < 4 * round && tail > 0 && 2 * tail <= round;
+}
+
+// Whether a launch of `rows` rows loads in the geometry's sequenced order
+// (which loads the N+1 tensors `seq` at a time, so a thread waits out
+// ceil((N+1)/seq) latencies in a row).  Below one round it does not (above).
+// Just past one round the rows beyond it run almost alone, each waiting out
+// its whole chain of latencies: with a chain of 8 or more, issuing all loads
+// at once is faster until the launch reaches one and a half rounds, from
+// where the sequenced order (one-row or strided kernel) catches up.  At
+// exactly one round the sequenced order still wins.  Measured on MI355X
+// (bf16, rotated past the MALL, us per launch, sequenced / all at once):
+//  * h = 8192, round 512, N = 8: T = 512 16.43 / 17.17; 520 22.06 / 19.92,
+//    544 22.28 / 20.27, 576 22.39 / 20.42, 600 22.16 / 20.47, 640 22.28 /
+//    20.61, 700 23.14 / 22.08, 736 23.91 / 23.52; 768 24.37 / 24.37, 800
+//    26.42 / 26.39.  N = 12, T = 600: 30.83 / 27.04; N = 16, T = 544: 39.47 /
+//    33.14, 700 40.38 / 37.63.  Chains of 3-3.5: N = 5, T = 544 15.29 /
+//    15.51; N = 6, T = 600 16.81 / 17.11.
+//  * h = 4096, round 1024, N = 8: T = 1024 16.12 / 17.21; 1040 22.17 /
+//    18.74, 1088 22.29 / 18.50, 1280 22.73 / 20.29, 1400 23.97 / 22.25; 1536
+//    25.05 / 25.04.  N = 2, T = 1300: 11.36 / 11.60.
+//  * h = 16384, round 512, N = 8: T = 512 31.08 / 33.88; 576 45.87 / 40.30,
+//    640 46.37 / 41.77; 768 50.73 / 50.71.
+// Between two and four rounds the two orders stay within 2% of each other
+// either way (the strided kernel runs there), so the sequenced one is kept.
+// Those are launches alone, back to back.  With a GEMM writing one partial
+// before each fused launch, as in a layer, all at once saves 1.1-2.0 us at
+// 576-704 x 8192, 4.1 at 1100 x 4096 and 5.9 at 576 x 16384 (N = 8); right
+// after another fused launch the 640- and 704-row launches lose about 1.3 us
+// instead.  The rule follows the layer's case.
+constexpr bool use_sequenced_order(int64_t rows, int64_t round, int num_partials, int seq) {
+  if (seq <= 0 || rows < round) return false;
+  const int chain = (num_partials + 1 + seq - 1) / seq;
+  return !(chain >= 8 && rows > round && 2 * rows < 3 * round);
 }
 
 // Pacing of the sequenced load order: after adding a tensor, a wave pauses

@@ -629,23 +629,26 @@ def test_row_whose_sum_of_squares_overflows_float32():
     check(rout[[0, 2]], x, "bf16", "residual_out, other rows")
 
 
-@pytest.mark.parametrize("h,N,dtype", [(8192, 5, "bf16"), (8192, 6, "bf16"), (8192, 8, "bf16"),
-                                       (8192, 16, "bf16"), (4096, 2, "bf16"), (4096, 8, "bf16"),
-                                       (8184, 8, "bf16"), (12296, 3, "bf16"), (16384, 8, "bf16"),
-                                       (3080, 4, "bf16"),
-                                       (4096, 8, "f32"), (2048, 3, "f32"), (8192, 2, "f32"),
-                                       (4092, 7, "f32")])
-def test_load_order_never_changes_a_bit(h, N, dtype):
+@pytest.mark.parametrize("h,N,dtype,T", [(8192, 5, "bf16", 1100), (8192, 6, "bf16", 1100),
+                                         (8192, 8, "bf16", 1100), (8192, 16, "bf16", 1100),
+                                         (4096, 2, "bf16", 1100), (4096, 8, "bf16", 1600),
+                                         (8184, 8, "bf16", 1100), (12296, 3, "bf16", 1100),
+                                         (16384, 8, "bf16", 1100), (3080, 4, "bf16", 1100),
+                                         (4096, 8, "f32", 1100), (2048, 3, "f32", 1100),
+                                         (8192, 2, "f32", 1100), (4092, 7, "f32", 1100)])
+def test_load_order_never_changes_a_bit(h, N, dtype, T):
     # A launch that fills every CU loads the tensors in summation order; a
     # smaller one (here each of the N shards) issues all loads at once.  The
     # arithmetic is the same, so every row must come out bit-identical, and
     # both must meet the oracle.
-    # Above one full round of workgroups at every width here (512 rows for the
-    # 1024-thread classes, 1024 rows for 512 x 1), with a last round at most
-    # half full, so the full launch takes the strided kernel where the width
-    # has one (not h = 16384 or 12296 bf16, nor 8192 f32); the ragged widths (8184,
-    # 12296, 3080) leave lanes that clamp their address inside the sequence.
-    T = 1100
+    # T is above one full round of workgroups at every width here (512 rows
+    # for the 1024-thread classes, 1024 rows for 512 x 1) and past the window
+    # just above one round where launches with a long sequence per thread
+    # issue all loads at once (hence 1600 rows for h = 4096, N = 8).  Where
+    # the last round is at most half full the full launch takes the strided
+    # kernel (not h = 16384 or 12296 bf16, nor 8192 f32); the ragged widths
+    # (8184, 12296, 3080) leave lanes that clamp their address inside the
+    # sequence.
     d = make_inputs("llama70b" if dtype == "bf16" else "tiny", num_tokens=T, hidden=h, seed=40 + N)
     # N partials: the drawn ones, then copies with their rows in reverse order.
     d["partials"] = np.concatenate([d["partials"]] + [d["partials"][:, ::-1]] * 8)[:N]
@@ -665,30 +668,34 @@ def test_load_order_never_changes_a_bit(h, N, dtype):
     check(rout[rows], x, dtype, "residual_out")
 
 
-# Launches of one to four rounds of rows whose last round is at most half full
-# run one round of workgroups that each take every round-th row (one round:
-# 512 workgroups for the 1024-thread class, h = 8192 bf16 or 4096 f32; 1024
-# for the 512 x 1 class, h = 4096 bf16).  (h, N, dtype, T) below fall in that
-# window; N = 5 loads two tensors ahead, the others one; 8184 and 4088 leave
-# lanes that clamp their address.
-STRIDED = [(8192, 8, "bf16", 768), (8192, 5, "bf16", 600), (8192, 16, "bf16", 1280),
-           (8184, 7, "bf16", 700), (4096, 8, "bf16", 1280), (4096, 2, "bf16", 1536),
-           (4088, 3, "bf16", 1100), (4096, 8, "f32", 640), (4096, 12, "f32", 1700)]
+# Launches whose row count is not a whole number of rounds (a round: 512
+# workgroups for the 1024-thread classes, h = 8192 or 16384 bf16 and 4096 or
+# 8192 f32; 1024 for 512 x 1, h = 4096 bf16).  The first nine cases have a
+# last round at most half full within four rounds and run the strided kernel
+# (N = 5 loads two tensors ahead, the others one; 8184 and 4088 leave lanes
+# that clamp their address).  The last five lie between one and one and a
+# half rounds with at least 8 tensors in each thread's sequence, and issue all
+# loads at once.
+RAGGED_ROUNDS = [(8192, 8, "bf16", 768), (8192, 5, "bf16", 600), (8192, 16, "bf16", 1280),
+           (8184, 7, "bf16", 1200), (4096, 8, "bf16", 1536), (4096, 2, "bf16", 1536),
+           (4088, 3, "bf16", 1100), (4096, 8, "f32", 1100), (4096, 12, "f32", 1700),
+           (8192, 8, "bf16", 600), (8184, 16, "bf16", 544), (4096, 8, "bf16", 1100),
+           (16384, 8, "bf16", 576), (8192, 7, "f32", 600)]
 
 
-@pytest.mark.parametrize("h,N,dtype,T", STRIDED)
-def test_strided_launch_matches_one_row_launches_and_oracle(h, N, dtype, T):
+@pytest.mark.parametrize("h,N,dtype,T", RAGGED_ROUNDS)
+def test_ragged_round_launch_matches_whole_round_launches_and_oracle(h, N, dtype, T):
     d = make_inputs("llama70b" if dtype == "bf16" else "tiny", num_tokens=T, hidden=h, seed=70 + N)
     d["partials"] = np.concatenate([d["partials"]] + [d["partials"][:, ::-1]] * 8)[:N]
     parts, res, w = upload(d)
     round_rows = 1024 if (h * (2 if dtype == "bf16" else 4)) <= 8192 else 512
     whole = (T // round_rows) * round_rows
-    say(f"strided: T={T} h={h} N={N} {dtype}; pieces [0,{whole}) and [{whole},{T})")
+    say(f"ragged rounds: T={T} h={h} N={N} {dtype}; pieces [0,{whole}) and [{whole},{T})")
     out = torch.full_like(res, float("nan"))
     rout = torch.full_like(res, float("nan"))
     tw.tw_fused_reduce_rmsnorm(parts, res, w, d["eps"], out=out, residual_out=rout)
-    # The same rows as whole rounds of one-row workgroups plus the remainder,
-    # which is too small for the sequenced order and issues all loads at once.
+    # The same rows as whole rounds of one-row workgroups, loaded in sequence,
+    # plus the remainder, which is under one round and issues all loads at once.
     out_p = torch.full_like(res, float("nan"))
     rout_p = torch.full_like(res, float("nan"))
     for lo, hi in ((0, whole), (whole, T)):
