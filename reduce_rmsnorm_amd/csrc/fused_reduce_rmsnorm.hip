@@ -484,8 +484,6 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
   hipError_t e;
   if (L.max_workgroups <= 0 || L.max_workgroups >= L.num_rows) {
     const int64_t round = seq_min_workgroups(block);
-    const bool seq = use_sequenced_order(L.num_rows, round, L.num_partials, geo.seq);
-    const KernelFn strided_fn = kStridedTable[bf16][g][L.num_partials - 1];
     // Dispatches over consecutive row ranges of about equal size, each within
     // the byte and work-item limits; the per-row code is the same in each.
     const int64_t row_bytes = (int64_t)(L.num_partials + 3) * nvec * 16;
@@ -497,9 +495,17 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
       const int64_t n = L.num_rows - r0 < chunk ? L.num_rows - r0 : chunk;
       k.row_begin = L.row_begin + r0;
       k.row_end = k.row_begin + n;
-      const bool strided = seq && strided_fn != nullptr && use_strided_grid(n, round);
-      const KernelFn fn = strided ? strided_fn : kTable[bf16][seq][g][L.num_partials - 1];
-      const int64_t grid = strided ? round : n;
+      // Each dispatch takes its own kernel for its row count (geometry.h).
+      const RowKernel rk = fused_row_kernel(g, L.num_partials, n);
+      const KernelFn fn =
+          rk == RowKernel::kStrided
+              ? kStridedTable[bf16][g][L.num_partials - 1]
+              : kTable[bf16][rk == RowKernel::kSequenced][g][L.num_partials - 1];
+      if (fn == nullptr) {
+        std::snprintf(err, errlen, "internal: no strided kernel for this row class");
+        return (int)hipErrorInvalidValue;
+      }
+      const int64_t grid = rk == RowKernel::kStrided ? round : n;
       const u32x4* first = k.partials[0];
       int64_t row_begin = k.row_begin;
       int32_t nvec32 = k.nvec;

@@ -138,6 +138,19 @@ constexpr bool use_sequenced_order(int64_t rows, int64_t round, int num_partials
   return !(chain >= 8 && rows > round && 2 * rows < 3 * round);
 }
 
+// The kernel one dispatch of `rows` rows of row class g with n partials
+// runs: one workgroup per row with all loads at once, one workgroup per row
+// in the sequenced order, or the strided kernel (which exists for the
+// sequenced geometries that load all vector slots in one sequence).
+enum class RowKernel { kAllAtOnce, kSequenced, kStrided };
+constexpr RowKernel fused_row_kernel(int g, int n, int64_t rows) {
+  const Geometry geo = fused_geometry(g, n);
+  const int64_t round = seq_min_workgroups(geo.block);
+  if (!use_sequenced_order(rows, round, n, geo.seq)) return RowKernel::kAllAtOnce;
+  if (geo.chunk == geo.vpt && use_strided_grid(rows, round)) return RowKernel::kStrided;
+  return RowKernel::kSequenced;
+}
+
 // Pacing of the sequenced load order: after adding a tensor, a wave pauses
 // for PACE * 64 clocks (s_sleep) before it requests the next one.  Fewer
 // requests in flight across the chip let HBM work more efficiently, and the

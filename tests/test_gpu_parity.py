@@ -711,6 +711,38 @@ def test_ragged_round_launch_matches_whole_round_launches_and_oracle(h, N, dtype
     check(ro[rows], x, dtype, "residual_out")
 
 
+@pytest.mark.parametrize("h,N,T", [(8192, 16, 3300), (16384, 16, 2100)])
+def test_each_dispatch_of_a_long_call_takes_its_own_kernel(h, N, T):
+    # A call over 768 MiB of traffic is cut into dispatches of about equal
+    # size, each a launch of its own: 2 x 1650 rows at h = 8192 (the strided
+    # kernel) and 3 x 700 rows at h = 16384 (all loads at once, being between
+    # one and one and a half rounds), with 16 partials.  Bit for bit against
+    # one launch per shard (all loads at once), and sampled rows, on both
+    # sides of every dispatch boundary, against the oracle.
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12)
+    parts = (torch.randn(N, T, h, device="cuda", generator=g, dtype=torch.bfloat16) * 0.5)
+    res = torch.randn(T, h, device="cuda", generator=g, dtype=torch.bfloat16)
+    w = (1 + 0.05 * torch.randn(h, device="cuda", generator=g)).to(torch.bfloat16)
+    eps = 1e-5
+    say(f"long call: T={T} h={h} N={N}")
+    out, rout = tw.tw_fused_reduce_rmsnorm(parts, res, w, eps)
+    out_s = torch.full_like(res, float("nan"))
+    rout_s = torch.full_like(res, float("nan"))
+    for k in range(N):
+        tw.tw_shard_rmsnorm(parts, res, w, eps, shard_index=k, out=out_s, residual_out=rout_s)
+    torch.cuda.synchronize()
+    assert torch.equal(out_s, out) and torch.equal(rout_s, rout)
+    piece = 1650 if h == 8192 else 700
+    idx = np.unique(np.concatenate([np.arange(0, T, 97), np.arange(T - 3, T)] +
+                                   [np.arange(b - 3, b + 3) for b in range(piece, T, piece)]))
+    ti = torch.from_numpy(idx).to("cuda")
+    y, x, _ = oracle.fused_reduce_rmsnorm([to_host(parts[i].index_select(0, ti)) for i in range(N)],
+                                          to_host(res.index_select(0, ti)), to_host(w), eps, "bf16")
+    check(to_host(out.index_select(0, ti)), y, "bf16", "out")
+    check(to_host(rout.index_select(0, ti)), x, "bf16", "residual_out")
+
+
 @pytest.mark.parametrize("eps", [0.0, 1e-12, 1e-5, 1.0])
 def test_subnormal_tiny_and_huge_rows_with_extreme_eps(eps):
     # Row 0: subnormal bf16 inputs (float32 subnormals once widened), where
