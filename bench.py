@@ -808,7 +808,12 @@ def main():
                 piece_sets.append([tw.PreparedFused([p[lo:hi] for p in parts], res[lo:hi], w,
                                                     wl.eps, out[lo:hi], rout[lo:hi], stream)
                                    for lo, hi in pieces])
-            for i in range(20):
+            # Each offset is warmed for about 50 ms of work: its prepared
+            # launches are built on the host first, and a GPU that has just
+            # waited needs tens of milliseconds of load to return to its
+            # steady clocks.
+            est = step_bytes / 6.0e12 + 3e-6 * len(piece_sets[0])
+            for i in range(max(20, math.ceil(0.05 / est))):
                 for launch in piece_sets[i % R]:
                     launch()
             torch.cuda.synchronize()
