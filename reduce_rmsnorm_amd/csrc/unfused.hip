@@ -268,8 +268,11 @@ int launch_reduce(const ReduceLaunch& L, char* err, size_t errlen) {
   k.reduced = static_cast<u32x4*>(L.reduced);
   k.nvec = (int32_t)nvec;
   const Geometry geo = fused_geometry(g, L.num_partials);
-  const ReduceFn fn =
-      kReduce[bf16][L.num_rows >= seq_min_workgroups(geo.block)][g][L.num_partials - 1];
+  // The fused kernel's rule for the load order, for a chain of N tensors
+  // (the reduce reads no residual).
+  const bool seq = use_sequenced_order(L.num_rows, seq_min_workgroups(geo.block),
+                                       L.num_partials - 1, geo.seq);
+  const ReduceFn fn = kReduce[bf16][seq][g][L.num_partials - 1];
   // Row ranges of at most max_rows_per_dispatch rows, each its own dispatch
   // with the tensors' base pointers advanced to the range's first row.
   const int64_t chunk = max_rows_per_dispatch(geo.block);
