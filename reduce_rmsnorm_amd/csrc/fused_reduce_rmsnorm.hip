@@ -26,7 +26,10 @@
 //    table (geometry.h) says which row classes and partial counts use the
 //    sequenced order; a launch too small to fill the CUs issues all loads at
 //    once regardless, since it would otherwise wait out one latency per
-//    tensor.  In the sequenced order a wave pauses briefly (s_sleep, a pace
+//    tensor, and so does a launch just past one round of workgroups with many
+//    tensors per row, whose extra rows would run almost alone.  A launch
+//    whose last round is at most half full runs the strided kernel below
+//    instead of one workgroup per row.  In the sequenced order a wave pauses briefly (s_sleep, a pace
 //    set per row class and N in geometry.h) after adding each tensor, before
 //    requesting the next: with many tensors per row, fewer requests in flight
 //    stream faster.  Out of range vectors (h not a multiple of

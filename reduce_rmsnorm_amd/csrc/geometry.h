@@ -75,8 +75,9 @@ constexpr Geometry fused_geometry(int g, int n) {
 // N = 8, h = 8192: 7.05 us against 9.34; h = 4096 at T = 512: 9.99 against
 // 11.05).  The crossover is one full round of workgroups: 256 CUs times the
 // workgroups that fit on a CU at 8 waves per SIMD (512 rows for 1024 x 1,
-// 1024 for 512 x 1).  Both orders do the same arithmetic, so the choice
-// never changes a bit of the result.
+// 1024 for 512 x 1); just past it, long chains of tensors still issue all
+// loads at once (use_sequenced_order below).  Both orders do the same
+// arithmetic, so the choice never changes a bit of the result.
 constexpr int kNumCUs = 256;
 constexpr int64_t seq_min_workgroups(int block) { return (int64_t)kNumCUs * (8 * 4 * 64 / block); }
 
