@@ -77,6 +77,8 @@ def parse():
                     help="override the workload's token count T (same distributions)")
     ap.add_argument("--partials", type=int, default=None,
                     help="override the workload's partial count N (same distributions)")
+    ap.add_argument("--hidden", type=int, default=None,
+                    help="override the workload's hidden size h (same distributions)")
     ap.add_argument("--no-split", dest="split", action="store_false",
                     help="keep every batch whole (one launch per step) whatever the planner says")
     ap.add_argument("--mode", choices=("full", "shard"), default="full",
@@ -595,11 +597,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = WORKLOADS[args.workload]
-    overridden = args.tokens is not None or args.partials is not None
+    overridden = args.tokens is not None or args.partials is not None or args.hidden is not None
     if overridden:
         import dataclasses
         wl = dataclasses.replace(wl, num_tokens=args.tokens or wl.num_tokens,
-                                 num_partials=args.partials or wl.num_partials)
+                                 num_partials=args.partials or wl.num_partials,
+                                 hidden=args.hidden or wl.hidden)
     T, h, N = wl.num_tokens, wl.hidden, wl.num_partials
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
 

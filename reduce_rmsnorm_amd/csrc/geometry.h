@@ -31,9 +31,21 @@ struct Geometry {
 //    at a time, 123.9 us (T = 2048); 1024 x 2 133.4 us; 256 x 8 132.1 us.
 // The occupancy cap applies up to N = 8 partials, where it costs no scratch;
 // with more partials the compiler's own allocation is kept.
+// Row widths between the powers of two get workgroups that fit them, one
+// vector per thread, so that no wave of a workgroup is empty and more of the
+// waves a CU holds carry data: 320 threads for up to 320 vectors (h = 2560
+// bf16; six workgroups per CU), 384 for up to 384 (h = 3072; five), 640 for up
+// to 640 (h = 5120; three, where two 1024-thread workgroups held six empty
+// waves each).  Measured at T = 1024, N = 8, us, the next larger class's
+// workgroup / the fitted one: h = 2560 12.97 / 11.24 (N = 2: 6.87 / 6.28,
+// N = 16: 22.03 / 17.58), h = 3072 14.22 / 13.04, h = 5120 23.32 / 20.75
+// (N = 16: 41.03 / 34.41; T = 4096: 86.64 / 83.48).  Below 7 partials the
+// 640-thread form is slower (h = 5120, N = 2: 11.60 / 12.31, N = 4: 15.55 /
+// 15.87, N = 5: 16.23 / 16.88), so those take the 512 x 2 class's geometry.
 constexpr Geometry kGeometry[] = {
-    {64, 1, 1, 1, 0},  {128, 1, 1, 1, 0}, {256, 1, 1, 1, 0},  {512, 1, 8, 1, 0},
-    {512, 2, 6, 2, 0}, {512, 4, 4, 2, 0}, {1024, 4, 1, 1, 0}, {1024, 8, 1, 1, 0}};
+    {64, 1, 1, 1, 0},  {128, 1, 1, 1, 0}, {256, 1, 1, 1, 0},  {320, 1, 8, 1, 0},
+    {384, 1, 8, 1, 0}, {512, 1, 8, 1, 0}, {640, 1, 8, 1, 0},  {512, 2, 6, 2, 0},
+    {512, 4, 4, 2, 0}, {1024, 4, 1, 1, 0}, {1024, 8, 1, 1, 0}};
 constexpr int kMaxCappedPartials = 8;
 
 // The geometry the fused kernels use for row class g and N partials.
@@ -63,6 +75,10 @@ constexpr int kMaxCappedPartials = 8;
 // occupancy cap; above it the cap is dropped (it would force spills).
 constexpr Geometry fused_geometry(int g, int n) {
   const Geometry k = kGeometry[g];
+  if (k.block == 640)                                   // below N = 7: the 512 x 2 class's choice
+    return n >= 7 ? Geometry{640, 1, 8, 1, 1} : n >= 5 ? Geometry{1024, 1, 8, 1, 2}
+                                                       : Geometry{512, 2, 6, 2, 0};
+  if ((k.block == 320 || k.block == 384) && n >= 2) return Geometry{k.block, 1, 8, 1, 1};
   if (k.block == 512 && k.vpt == 2 && n >= 5) return Geometry{1024, 1, 8, 1, n >= 7 ? 1 : 2};
   if (k.block == 512 && k.vpt == 1 && n >= 2) return Geometry{512, 1, 8, 1, 1};
   if (k.block == 512 && k.vpt == 4 && n >= 2) return Geometry{1024, 2, 8, 1, 1};
@@ -166,12 +182,18 @@ constexpr RowKernel fused_row_kernel(int g, int n, int64_t rows) {
 //  * 1024 x 2 class (h = 16384, T = 1024): N <= 4 best unpaced; N = 8 61.23
 //    against 60.04 (10), N = 16 103.48 against 97.44 (12).
 // Partial counts between the measured ones take the nearer measured pace.
+// The 320-, 384- and 640-thread classes take the pace of the form they
+// share (512 x 1 and 1024 x 1 respectively); they were not paced apart.
 constexpr int fused_pace(int g, int n) {
   const Geometry k = kGeometry[g];
   if (k.block == 512 && k.vpt == 2 && n >= 7)           // 1024 x 1, sequenced
     return n <= 8 ? 4 : n <= 10 ? 5 : n <= 12 ? 8 : 10;
   if (k.block == 512 && k.vpt == 1 && n >= 8)           // 512 x 1, sequenced
     return n <= 8 ? 8 : n <= 12 ? 10 : 12;
+  if ((k.block == 320 || k.block == 384) && n >= 8)     // as 512 x 1
+    return n <= 8 ? 8 : n <= 12 ? 10 : 12;
+  if (k.block == 640 && n >= 7)                         // as 1024 x 1
+    return n <= 8 ? 4 : n <= 10 ? 5 : n <= 12 ? 8 : 10;
   if (k.block == 512 && k.vpt == 4 && n >= 6)           // 1024 x 2, sequenced
     return n <= 6 ? 4 : n <= 12 ? 10 : 12;
   return 0;

@@ -635,7 +635,10 @@ def test_row_whose_sum_of_squares_overflows_float32():
                                          (8184, 8, "bf16", 1100), (12296, 3, "bf16", 1100),
                                          (16384, 8, "bf16", 1100), (3080, 4, "bf16", 1100),
                                          (4096, 8, "f32", 1100), (2048, 3, "f32", 1100),
-                                         (8192, 2, "f32", 1100), (4092, 7, "f32", 1100)])
+                                         (8192, 2, "f32", 1100), (4092, 7, "f32", 1100),
+                                         (5120, 8, "bf16", 1600), (5112, 16, "bf16", 1600),
+                                         (2560, 8, "bf16", 3200), (2552, 12, "bf16", 3200),
+                                         (3072, 2, "bf16", 1400), (1280, 4, "f32", 3100)])
 def test_load_order_never_changes_a_bit(h, N, dtype, T):
     # A launch that fills every CU loads the tensors in summation order; a
     # smaller one (here each of the N shards) issues all loads at once.  The
@@ -648,7 +651,9 @@ def test_load_order_never_changes_a_bit(h, N, dtype, T):
     # the last round is at most half full the full launch takes the strided
     # kernel (not h = 16384 or 12296 bf16, nor 8192 f32); the ragged widths
     # (8184, 12296, 3080) leave lanes that clamp their address inside the
-    # sequence.
+    # sequence.  h = 5120 (N >= 7), 2560, 3072 and f32 1280 run the 640-, 320-
+    # and 384-thread workgroups (rounds of 768, 1536 and 1280 rows), 5112 and
+    # 2552 with a lane that clamps.
     d = make_inputs("llama70b" if dtype == "bf16" else "tiny", num_tokens=T, hidden=h, seed=40 + N)
     # N partials: the drawn ones, then copies with their rows in reverse order.
     d["partials"] = np.concatenate([d["partials"]] + [d["partials"][:, ::-1]] * 8)[:N]
@@ -673,14 +678,33 @@ def test_load_order_never_changes_a_bit(h, N, dtype, T):
 # 8192 f32; 1024 for 512 x 1, h = 4096 bf16).  The first nine cases have a
 # last round at most half full within four rounds and run the strided kernel
 # (N = 5 loads two tensors ahead, the others one; 8184 and 4088 leave lanes
-# that clamp their address).  The last five lie between one and one and a
+# that clamp their address).  The other seven lie between one and one and a
 # half rounds with at least 8 tensors in each thread's sequence, and issue all
-# loads at once.
+# loads at once; the last two run the 640- and 320-thread workgroups (rounds
+# of 768 and 1536 rows).
 RAGGED_ROUNDS = [(8192, 8, "bf16", 768), (8192, 5, "bf16", 600), (8192, 16, "bf16", 1280),
            (8184, 7, "bf16", 1200), (4096, 8, "bf16", 1536), (4096, 2, "bf16", 1536),
            (4088, 3, "bf16", 1100), (4096, 8, "f32", 1100), (4096, 12, "f32", 1700),
            (8192, 8, "bf16", 600), (8184, 16, "bf16", 544), (4096, 8, "bf16", 1100),
-           (16384, 8, "bf16", 576), (8192, 7, "f32", 600)]
+           (16384, 8, "bf16", 576), (8192, 7, "f32", 600),
+           (5120, 16, "bf16", 800), (2560, 8, "bf16", 1700)]
+
+
+def _round_rows(h, elem_bytes, n):
+    """Rows one round of resident workgroups holds, for the sequenced row
+    classes these tests use."""
+    nvec = h * elem_bytes // 16
+    if nvec <= 320:
+        block = 320
+    elif nvec <= 384:
+        block = 384
+    elif nvec <= 512:
+        block = 512
+    elif nvec <= 640:
+        block = 640 if n >= 7 else 1024 if n >= 5 else 512
+    else:
+        block = 1024
+    return 256 * (2048 // block)
 
 
 @pytest.mark.parametrize("h,N,dtype,T", RAGGED_ROUNDS)
@@ -688,7 +712,7 @@ def test_ragged_round_launch_matches_whole_round_launches_and_oracle(h, N, dtype
     d = make_inputs("llama70b" if dtype == "bf16" else "tiny", num_tokens=T, hidden=h, seed=70 + N)
     d["partials"] = np.concatenate([d["partials"]] + [d["partials"][:, ::-1]] * 8)[:N]
     parts, res, w = upload(d)
-    round_rows = 1024 if (h * (2 if dtype == "bf16" else 4)) <= 8192 else 512
+    round_rows = _round_rows(h, 2 if dtype == "bf16" else 4, N)
     whole = (T // round_rows) * round_rows
     say(f"ragged rounds: T={T} h={h} N={N} {dtype}; pieces [0,{whole}) and [{whole},{T})")
     out = torch.full_like(res, float("nan"))
