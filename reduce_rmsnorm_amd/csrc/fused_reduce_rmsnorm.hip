@@ -379,13 +379,14 @@ using KernelFn = void (*)(const u32x4*, int64_t, int32_t, KArgs);
 using RowsKernelFn = void (*)(KArgs, int64_t, int64_t);
 
 // Kernel tables by [row class][N - 1].  SEQ_ORDER selects the geometry's own
-// load order; without it every entry loads all tensors at once (the same
-// arithmetic, for launches too small to fill the CUs).
+// load order; without it every entry takes the short form (all tensors at
+// once, or a few in flight for 512 x 3; the same arithmetic, for launches too
+// small to fill the CUs).
 constexpr int load_order(int g, int n, bool seq_order) {
-  return seq_order ? fused_geometry(g, n).seq : 0;
+  return seq_order ? fused_geometry(g, n).seq : short_form_depth(fused_geometry(g, n));
 }
 constexpr int load_pace(int g, int n, bool seq_order) {
-  return load_order(g, n, seq_order) > 0 ? fused_pace(g, n) : 0;
+  return seq_order && load_order(g, n, seq_order) > 0 ? fused_pace(g, n) : 0;
 }
 template <bool BF16, bool SEQ_ORDER, int G, int... Ns>
 constexpr std::array<KernelFn, sizeof...(Ns)> row_of(std::integer_sequence<int, Ns...>) {

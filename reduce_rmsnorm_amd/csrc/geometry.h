@@ -42,10 +42,17 @@ struct Geometry {
 // (N = 16: 41.03 / 34.41; T = 4096: 86.64 / 83.48).  Below 7 partials the
 // 640-thread form is slower (h = 5120, N = 2: 11.60 / 12.31, N = 4: 15.55 /
 // 15.87, N = 5: 16.23 / 16.88), so those take the 512 x 2 class's geometry.
+// Likewise 1025-1536 vectors (h = 9216-12288 bf16) run 512 x 3 from N = 6 on,
+// one vector slot at a time in sequence, four workgroups per CU, where 1024 x
+// 2 left half its threads without a second vector: N = 8, T = 1024, us, 1024
+// x 2 / 512 x 3: h = 12288 51.26 / 47.58 (N = 16: 87.18 / 76.29; T = 4096:
+// 200.06 / 190.11), h = 10240 47.94 / 41.74, h = 9216 46.87 / 39.92; N = 6
+// 41.12 / 41.02; below N = 6 it was slower (N = 2: 23.71 / 24.08, N = 4: 32.14
+// / 33.00) and 1024 x 2 is kept.
 constexpr Geometry kGeometry[] = {
     {64, 1, 1, 1, 0},  {128, 1, 1, 1, 0}, {256, 1, 1, 1, 0},  {320, 1, 8, 1, 0},
     {384, 1, 8, 1, 0}, {512, 1, 8, 1, 0}, {640, 1, 8, 1, 0},  {512, 2, 6, 2, 0},
-    {512, 4, 4, 2, 0}, {1024, 4, 1, 1, 0}, {1024, 8, 1, 1, 0}};
+    {512, 3, 4, 1, 0}, {512, 4, 4, 2, 0}, {1024, 4, 1, 1, 0}, {1024, 8, 1, 1, 0}};
 constexpr int kMaxCappedPartials = 8;
 
 // The geometry the fused kernels use for row class g and N partials.
@@ -79,6 +86,9 @@ constexpr Geometry fused_geometry(int g, int n) {
     return n >= 7 ? Geometry{640, 1, 8, 1, 1} : n >= 5 ? Geometry{1024, 1, 8, 1, 2}
                                                        : Geometry{512, 2, 6, 2, 0};
   if ((k.block == 320 || k.block == 384) && n >= 2) return Geometry{k.block, 1, 8, 1, 1};
+  if (k.block == 512 && k.vpt == 3)                     // below N = 6: the 512 x 4 class's choice
+    return n >= 6 ? Geometry{512, 3, 8, 1, 1} : n >= 2 ? Geometry{1024, 2, 8, 1, 1}
+                                                       : Geometry{512, 4, 4, 2, 0};
   if (k.block == 512 && k.vpt == 2 && n >= 5) return Geometry{1024, 1, 8, 1, n >= 7 ? 1 : 2};
   if (k.block == 512 && k.vpt == 1 && n >= 2) return Geometry{512, 1, 8, 1, 1};
   if (k.block == 512 && k.vpt == 4 && n >= 2) return Geometry{1024, 2, 8, 1, 1};
@@ -168,6 +178,16 @@ constexpr RowKernel fused_row_kernel(int g, int n, int64_t rows) {
   return RowKernel::kSequenced;
 }
 
+// The depth of the short form of a geometry's load order, the one launches
+// too small for the sequenced order take: 0 issues all N+1 loads of a chunk at
+// once.  512 x 3 keeps three tensors in flight per vector slot instead, since
+// all of them would not fit in registers beside the three slots' sums (that
+// form spilled and took 11.72 against 10.45 us at 128 rows x 12288, N = 8;
+// three in flight took 10.73, and 13.99 against 14.47 at 256 rows).
+constexpr int short_form_depth(const Geometry& geo) {
+  return geo.block == 512 && geo.vpt == 3 ? 3 : 0;
+}
+
 // Pacing of the sequenced load order: after adding a tensor, a wave pauses
 // for PACE * 64 clocks (s_sleep) before it requests the next one.  Fewer
 // requests in flight across the chip let HBM work more efficiently, and the
@@ -182,8 +202,9 @@ constexpr RowKernel fused_row_kernel(int g, int n, int64_t rows) {
 //  * 1024 x 2 class (h = 16384, T = 1024): N <= 4 best unpaced; N = 8 61.23
 //    against 60.04 (10), N = 16 103.48 against 97.44 (12).
 // Partial counts between the measured ones take the nearer measured pace.
-// The 320-, 384- and 640-thread classes take the pace of the form they
-// share (512 x 1 and 1024 x 1 respectively); they were not paced apart.
+// The 320-, 384- and 640-thread classes and 512 x 3 take the pace of the
+// form they share (512 x 1, 1024 x 1 and 1024 x 2 respectively); they were not
+// paced apart.
 constexpr int fused_pace(int g, int n) {
   const Geometry k = kGeometry[g];
   if (k.block == 512 && k.vpt == 2 && n >= 7)           // 1024 x 1, sequenced
@@ -192,6 +213,8 @@ constexpr int fused_pace(int g, int n) {
     return n <= 8 ? 8 : n <= 12 ? 10 : 12;
   if ((k.block == 320 || k.block == 384) && n >= 8)     // as 512 x 1
     return n <= 8 ? 8 : n <= 12 ? 10 : 12;
+  if (k.block == 512 && k.vpt == 3 && n >= 6)           // as 1024 x 2
+    return n <= 6 ? 4 : n <= 12 ? 10 : 12;
   if (k.block == 640 && n >= 7)                         // as 1024 x 1
     return n <= 8 ? 4 : n <= 10 ? 5 : n <= 12 ? 8 : 10;
   if (k.block == 512 && k.vpt == 4 && n >= 6)           // 1024 x 2, sequenced

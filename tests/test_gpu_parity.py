@@ -638,7 +638,8 @@ def test_row_whose_sum_of_squares_overflows_float32():
                                          (8192, 2, "f32", 1100), (4092, 7, "f32", 1100),
                                          (5120, 8, "bf16", 1600), (5112, 16, "bf16", 1600),
                                          (2560, 8, "bf16", 3200), (2552, 12, "bf16", 3200),
-                                         (3072, 2, "bf16", 1400), (1280, 4, "f32", 3100)])
+                                         (3072, 2, "bf16", 1400), (1280, 4, "f32", 3100),
+                                         (12288, 8, "bf16", 2200), (12280, 16, "bf16", 2200)])
 def test_load_order_never_changes_a_bit(h, N, dtype, T):
     # A launch that fills every CU loads the tensors in summation order; a
     # smaller one (here each of the N shards) issues all loads at once.  The
@@ -653,7 +654,8 @@ def test_load_order_never_changes_a_bit(h, N, dtype, T):
     # (8184, 12296, 3080) leave lanes that clamp their address inside the
     # sequence.  h = 5120 (N >= 7), 2560, 3072 and f32 1280 run the 640-, 320-
     # and 384-thread workgroups (rounds of 768, 1536 and 1280 rows), 5112 and
-    # 2552 with a lane that clamps.
+    # 2552 with a lane that clamps; 12288 and 12280 run 512 x 3, whose short
+    # form (the shards) keeps three tensors in flight per vector slot.
     d = make_inputs("llama70b" if dtype == "bf16" else "tiny", num_tokens=T, hidden=h, seed=40 + N)
     # N partials: the drawn ones, then copies with their rows in reverse order.
     d["partials"] = np.concatenate([d["partials"]] + [d["partials"][:, ::-1]] * 8)[:N]
@@ -680,14 +682,15 @@ def test_load_order_never_changes_a_bit(h, N, dtype, T):
 # (N = 5 loads two tensors ahead, the others one; 8184 and 4088 leave lanes
 # that clamp their address).  The other seven lie between one and one and a
 # half rounds with at least 8 tensors in each thread's sequence, and issue all
-# loads at once; the last two run the 640- and 320-thread workgroups (rounds
-# of 768 and 1536 rows).
+# loads at once; of the last three, two run the 640- and 320-thread
+# workgroups (rounds of 768 and 1536 rows) and one 512 x 3 (1024 rows, its
+# short form keeping three tensors in flight).
 RAGGED_ROUNDS = [(8192, 8, "bf16", 768), (8192, 5, "bf16", 600), (8192, 16, "bf16", 1280),
            (8184, 7, "bf16", 1200), (4096, 8, "bf16", 1536), (4096, 2, "bf16", 1536),
            (4088, 3, "bf16", 1100), (4096, 8, "f32", 1100), (4096, 12, "f32", 1700),
            (8192, 8, "bf16", 600), (8184, 16, "bf16", 544), (4096, 8, "bf16", 1100),
            (16384, 8, "bf16", 576), (8192, 7, "f32", 600),
-           (5120, 16, "bf16", 800), (2560, 8, "bf16", 1700)]
+           (5120, 16, "bf16", 800), (2560, 8, "bf16", 1700), (12288, 8, "bf16", 1100)]
 
 
 def _round_rows(h, elem_bytes, n):
@@ -702,6 +705,8 @@ def _round_rows(h, elem_bytes, n):
         block = 512
     elif nvec <= 640:
         block = 640 if n >= 7 else 1024 if n >= 5 else 512
+    elif 1024 < nvec <= 1536 and n >= 6:
+        block = 512
     else:
         block = 1024
     return 256 * (2048 // block)

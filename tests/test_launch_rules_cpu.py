@@ -5,8 +5,8 @@ measured on MI355X.  tests/c/launch_rules.cpp is built with the host
 compiler against the launcher's geometry header; no GPU.
 
 A round is the number of workgroups resident at once: 512 for the
-1024-thread geometries, 1024 for 512 x 1, 768 for 640 x 1, 1280 for 384 x 1
-and 1536 for 320 x 1.  The rules:
+1024-thread geometries, 1024 for 512 x 1 and 512 x 3, 768 for 640 x 1, 1280
+for 384 x 1 and 1536 for 320 x 1.  The rules:
 * below one round, all loads at once (too few rows to fill the CUs);
 * between one and one and a half rounds, all loads at once when each thread
   waits on a chain of 8 or more tensors (N + 1 tensors, one or two in
@@ -62,6 +62,10 @@ CASES = {
     (5120, 2, 8, 768): "seq", (5120, 2, 8, 800): "all", (5120, 2, 8, 1600): "strided",
     (5120, 2, 7, 1100): "all", (5120, 2, 6, 1100): "strided", (5120, 2, 4, 1100): "all",
     (1280, 4, 4, 3100): "strided", (1280, 4, 8, 1600): "all",
+    # 1025-1536 vectors: 512 x 3 from N = 6 on (no strided kernel: one slot at
+    # a time), 1024 x 2 below
+    (12288, 2, 8, 1024): "seq", (12288, 2, 8, 1100): "all", (12288, 2, 8, 2200): "seq",
+    (12288, 2, 8, 256): "all", (12288, 2, 4, 1100): "seq", (9216, 2, 16, 1600): "seq",
     # narrow and wide rows never load in sequence
     (512, 4, 2, 64): "all", (2048, 2, 8, 100000): "all", (32768, 2, 8, 4096): "all",
 }
@@ -96,13 +100,15 @@ def test_round_sizes(rules_exe):
     # (threads, vectors per thread) and the rows one round holds
     got = _run(rules_exe, [(8192, 2, 8, 1), (4096, 2, 8, 1), (16384, 2, 8, 1), (8192, 2, 4, 1),
                            (2560, 2, 8, 1), (3072, 2, 8, 1), (5120, 2, 8, 1), (5120, 2, 6, 1),
-                           (5120, 2, 4, 1), (5112, 2, 16, 1), (2552, 2, 1, 1)])
+                           (5120, 2, 4, 1), (5112, 2, 16, 1), (2552, 2, 1, 1),
+                           (12288, 2, 8, 1), (12288, 2, 4, 1), (12288, 2, 1, 1)])
     assert [g[1:] for g in got] == [["1024", "1", "512"], ["512", "1", "1024"],
                                     ["1024", "2", "512"], ["512", "2", "1024"],
                                     ["320", "1", "1536"], ["384", "1", "1280"],
                                     ["640", "1", "768"], ["1024", "1", "512"],
                                     ["512", "2", "1024"], ["640", "1", "768"],
-                                    ["320", "1", "1536"]]
+                                    ["320", "1", "1536"], ["512", "3", "1024"],
+                                    ["1024", "2", "512"], ["512", "4", "1024"]]
 
 
 def test_strided_kernel_only_within_four_rounds_with_a_short_last_round(rules_exe):
