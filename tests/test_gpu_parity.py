@@ -799,11 +799,15 @@ def test_subnormal_tiny_and_huge_rows_with_extreme_eps(eps):
     check(out[rows], y, "bf16", "out")
 
 
-@pytest.mark.parametrize("N,T,h", [(12, 600, 8192), (16, 1100, 4096), (16, 520, 16384), (3, 40, 8192)])
+@pytest.mark.parametrize("N,T,h", [(12, 600, 8192), (16, 1100, 4096), (16, 520, 16384), (3, 40, 8192),
+                                   (8, 1700, 2560), (2, 1400, 3072), (8, 900, 5120), (8, 1300, 12288),
+                                   (16, 200, 12280)])
 def test_unfused_comparator_many_partials(N, T, h):
     # The comparator's reduce step uses the fused geometry and load orders
     # (sequenced above one full round of workgroups), with no occupancy cap
-    # above ten partials.
+    # above ten partials; its add + RMSNorm step takes the row class's base
+    # workgroup, which for h = 2560, 3072, 5120 and 12288 is the fitted one
+    # (320, 384, 640 threads, 512 x 3).
     d = make_inputs("llama70b", num_tokens=T, hidden=h, seed=60 + N)
     d["partials"] = np.concatenate([d["partials"], d["partials"][:, ::-1]])[:N]
     parts, res, w = upload(d)
