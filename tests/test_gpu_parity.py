@@ -639,7 +639,8 @@ def test_row_whose_sum_of_squares_overflows_float32():
                                          (5120, 8, "bf16", 1600), (5112, 16, "bf16", 1600),
                                          (2560, 8, "bf16", 3200), (2552, 12, "bf16", 3200),
                                          (3072, 2, "bf16", 1400), (1280, 4, "f32", 3100),
-                                         (12288, 8, "bf16", 2200), (12280, 16, "bf16", 2200)])
+                                         (12288, 8, "bf16", 2200), (12280, 16, "bf16", 2200),
+                                         (2560, 1, "bf16", 1100), (1536, 1, "f32", 1100)])
 def test_load_order_never_changes_a_bit(h, N, dtype, T):
     # A launch that fills every CU loads the tensors in summation order; a
     # smaller one (here each of the N shards) issues all loads at once.  The
@@ -655,7 +656,9 @@ def test_load_order_never_changes_a_bit(h, N, dtype, T):
     # sequence.  h = 5120 (N >= 7), 2560, 3072 and f32 1280 run the 640-, 320-
     # and 384-thread workgroups (rounds of 768, 1536 and 1280 rows), 5112 and
     # 2552 with a lane that clamps; 12288 and 12280 run 512 x 3, whose short
-    # form (the shards) keeps three tensors in flight per vector slot.
+    # form (the shards) keeps three tensors in flight per vector slot.  With
+    # one partial the 320- and 384-thread classes issue all loads at once in
+    # every launch (N = 1 has no sequenced order).
     d = make_inputs("llama70b" if dtype == "bf16" else "tiny", num_tokens=T, hidden=h, seed=40 + N)
     # N partials: the drawn ones, then copies with their rows in reverse order.
     d["partials"] = np.concatenate([d["partials"]] + [d["partials"][:, ::-1]] * 8)[:N]
