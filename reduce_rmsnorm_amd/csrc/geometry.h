@@ -82,10 +82,11 @@ constexpr int kMaxCappedPartials = 8;
 // occupancy cap; above it the cap is dropped (it would force spills).
 constexpr Geometry fused_geometry(int g, int n) {
   const Geometry k = kGeometry[g];
-  if (k.block == 640)                                   // below N = 7: the 512 x 2 class's choice
+  if (k.block == 640 && k.vpt == 1)                     // below N = 7: the 512 x 2 class's choice
     return n >= 7 ? Geometry{640, 1, 8, 1, 1} : n >= 5 ? Geometry{1024, 1, 8, 1, 2}
                                                        : Geometry{512, 2, 6, 2, 0};
-  if ((k.block == 320 || k.block == 384) && n >= 2) return Geometry{k.block, 1, 8, 1, 1};
+  if ((k.block == 320 || k.block == 384) && k.vpt == 1 && n >= 2)
+    return Geometry{k.block, 1, 8, 1, 1};
   if (k.block == 512 && k.vpt == 3)                     // below N = 6: the 512 x 4 class's choice
     return n >= 6 ? Geometry{512, 3, 8, 1, 1} : n >= 2 ? Geometry{1024, 2, 8, 1, 1}
                                                        : Geometry{512, 4, 4, 2, 0};
@@ -211,11 +212,11 @@ constexpr int fused_pace(int g, int n) {
     return n <= 8 ? 4 : n <= 10 ? 5 : n <= 12 ? 8 : 10;
   if (k.block == 512 && k.vpt == 1 && n >= 8)           // 512 x 1, sequenced
     return n <= 8 ? 8 : n <= 12 ? 10 : 12;
-  if ((k.block == 320 || k.block == 384) && n >= 8)     // as 512 x 1
+  if ((k.block == 320 || k.block == 384) && k.vpt == 1 && n >= 8)  // as 512 x 1
     return n <= 8 ? 8 : n <= 12 ? 10 : 12;
   if (k.block == 512 && k.vpt == 3 && n >= 6)           // as 1024 x 2
     return n <= 6 ? 4 : n <= 12 ? 10 : 12;
-  if (k.block == 640 && n >= 7)                         // as 1024 x 1
+  if (k.block == 640 && k.vpt == 1 && n >= 7)           // as 1024 x 1
     return n <= 8 ? 4 : n <= 10 ? 5 : n <= 12 ? 8 : 10;
   if (k.block == 512 && k.vpt == 4 && n >= 6)           // 1024 x 2, sequenced
     return n <= 6 ? 4 : n <= 12 ? 10 : 12;
