@@ -203,21 +203,26 @@ constexpr int short_form_depth(const Geometry& geo) {
 //  * 1024 x 2 class (h = 16384, T = 1024): N <= 4 best unpaced; N = 8 61.23
 //    against 60.04 (10), N = 16 103.48 against 97.44 (12).
 // Partial counts between the measured ones take the nearer measured pace.
-// The 320-, 384- and 640-thread classes and 512 x 3 take the pace of the
-// form they share (512 x 1, 1024 x 1 and 1024 x 2 respectively); they were not
-// paced apart.
+// The fitted classes hold more workgroups per CU, and the pause that suits
+// the power-of-two classes slows them (T = 4096, us, unpaced / half the
+// 512 x 1 or 1024 x 1 pause / the full one): 640 threads (h = 5120), N = 7
+// 72.99 / 74.26 / 75.96, N = 12 108.13 / 112.30 / 118.50, N = 16 135.13 /
+// 144.02 / 156.58; 320 threads (h = 2560), N = 8 39.71 / 40.91 / 42.91, N = 16
+// 65.57 / 69.64 / 77.10; 384 threads (h = 3072), N = 8 46.69 / 46.93 / 47.38,
+// N = 12 63.29 / 62.98 / 63.95, N = 16 79.79 / 78.54 / 81.64.  So 320 and 640
+// run unpaced and 384 takes half of 512 x 1's pause.  512 x 3 keeps 1024 x 2's
+// (h = 12288, N = 8, T = 1024: 49.58 / 48.89 / 47.54; N = 16 82.10 / 79.67 /
+// 76.14).
 constexpr int fused_pace(int g, int n) {
   const Geometry k = kGeometry[g];
   if (k.block == 512 && k.vpt == 2 && n >= 7)           // 1024 x 1, sequenced
     return n <= 8 ? 4 : n <= 10 ? 5 : n <= 12 ? 8 : 10;
   if (k.block == 512 && k.vpt == 1 && n >= 8)           // 512 x 1, sequenced
     return n <= 8 ? 8 : n <= 12 ? 10 : 12;
-  if ((k.block == 320 || k.block == 384) && k.vpt == 1 && n >= 8)  // as 512 x 1
-    return n <= 8 ? 8 : n <= 12 ? 10 : 12;
+  if (k.block == 384 && k.vpt == 1 && n >= 8)           // half of 512 x 1's
+    return n <= 8 ? 4 : n <= 12 ? 5 : 6;
   if (k.block == 512 && k.vpt == 3 && n >= 6)           // as 1024 x 2
     return n <= 6 ? 4 : n <= 12 ? 10 : 12;
-  if (k.block == 640 && k.vpt == 1 && n >= 7)           // as 1024 x 1
-    return n <= 8 ? 4 : n <= 10 ? 5 : n <= 12 ? 8 : 10;
   if (k.block == 512 && k.vpt == 4 && n >= 6)           // 1024 x 2, sequenced
     return n <= 6 ? 4 : n <= 12 ? 10 : 12;
   return 0;
