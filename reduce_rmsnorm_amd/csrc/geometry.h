@@ -39,7 +39,8 @@ struct Geometry {
 // waves each).  Measured at T = 1024, N = 8, us, the next larger class's
 // workgroup / the fitted one: h = 2560 12.97 / 11.24 (N = 2: 6.87 / 6.28,
 // N = 16: 22.03 / 17.58), h = 3072 14.22 / 13.04, h = 5120 23.32 / 20.75
-// (N = 16: 41.03 / 34.41; T = 4096: 86.64 / 83.48).  Below 7 partials the
+// (N = 16: 41.03 / 34.41; T = 4096, with the 1024 x 1 pause, 86.64 / 83.48;
+// unpaced, as fused_pace now has it, 80.16).  Below 7 partials the
 // 640-thread form is slower (h = 5120, N = 2: 11.60 / 12.31, N = 4: 15.55 /
 // 15.87, N = 5: 16.23 / 16.88), so those take the 512 x 2 class's geometry.
 // Likewise 1025-1536 vectors (h = 9216-12288 bf16) run 512 x 3 from N = 6 on,
