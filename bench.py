@@ -642,7 +642,7 @@ def main():
     # prepared once per rotated buffer set so the host costs one C call each.
     planner = tw.SplitPlanCache(**plan_kw)
     plan0 = planner(T)
-    if not args.split and plan0["reason"] == 0:
+    if not args.split and plan0["suffix_tokens"] > 0:
         plan0 = dict(plan0, prefix_tokens=T, suffix_tokens=0, offset=-1, reason=-1)
     def prepare(st):
         per_set = []
@@ -650,7 +650,7 @@ def main():
             if args.mode == "shard":
                 per_set.append([tw.PreparedFused(parts, res, w, wl.eps, out, rout, st,
                                                  mode="shard", shard_index=0)])
-            elif plan0["reason"] == 0:
+            elif plan0["suffix_tokens"] > 0:
                 P = plan0["prefix_tokens"]
                 per_set.append([
                     tw.PreparedFused([p[lo:hi] for p in parts], res[lo:hi], w, wl.eps,

@@ -54,7 +54,7 @@ typedef enum {
                                      for bf16, h <= 32768 for fp32 */
 #define TW_MAX_TOKENS 2147483647  /* largest num_tokens */
 
-#define TW_ABI_VERSION 1
+#define TW_ABI_VERSION 2
 
 /* Version of this ABI (TW_ABI_VERSION of the built library). */
 int32_t tw_abi_version(void);
@@ -231,6 +231,10 @@ typedef struct {
 #define TW_PLAN_SINGLE_WAVE 2
 #define TW_PLAN_NO_FEASIBLE_OFFSET 3
 #define TW_PLAN_EMPTY 4
+#define TW_PLAN_MEASURED_SPLIT 5        /* tw_split_plan_measured: the table's offset */
+#define TW_PLAN_MEASURED_UNSPLIT 6      /* tw_split_plan_measured: the table keeps T whole */
+#define TW_PLAN_MEASURED_OVER_WAVES 7   /* tw_split_plan_measured: the table's offset breaks
+                                           the wave condition, so T stays whole */
 
 typedef struct {
   int64_t prefix_tokens;
@@ -241,6 +245,8 @@ typedef struct {
   int32_t waves_suffix;
   int32_t reason;               /* one of TW_PLAN_* */
 } tw_split_plan_result;
+/* A plan splits exactly when suffix_tokens > 0 (reasons TW_PLAN_SPLIT and
+ * TW_PLAN_MEASURED_SPLIT); then prefix_tokens = floor(T/2) + offset. */
 
 /*
  * tw_split_plan -- host only, integer arithmetic, no device call.
@@ -250,6 +256,42 @@ typedef struct {
  * ctas_per_token_tile exceeds 2^20 or a wave count does not fit in int32.
  */
 tw_status tw_split_plan(const tw_split_problem* in, tw_split_plan_result* out);
+
+/*
+ * Measured split table.  [Blog] "Fix one" chooses the offset per shape by
+ * timing the two GEMMs offline and keeps the winner in a lookup table keyed
+ * by the shape.  One entry of such a table:
+ */
+typedef struct {
+  int64_t num_tokens;           /* T the entry applies to, >= 1 */
+  int32_t offset;               /* the measured winner: 0 <= offset < floor(T/2),
+                                   or -1 when the whole batch was fastest */
+} tw_split_entry;
+
+/*
+ * tw_split_plan_measured -- tw_split_plan with a measured table consulted
+ * first.  host only, integer arithmetic, no device call.
+ *   in            the problem, as for tw_split_plan (its offsets serve the
+ *                 analytic search of counts the table does not list)
+ *   table         table_len entries, token counts strictly ascending; the
+ *                 caller keeps ownership (the library keeps no pointer)
+ *   table_len     >= 0; 0 (table may be NULL) gives exactly tw_split_plan
+ *   out           non-NULL
+ * In the pages' order: T == 0, T < min_split_tokens and waves(T) <= 1 keep
+ * the batch whole, as in tw_split_plan, before the table is read.  A T the
+ * table lists then takes the table's offset: -1 keeps it whole
+ * (TW_PLAN_MEASURED_UNSPLIT); an offset whose pieces take no more waves than
+ * the whole batch splits at prefix = floor(T/2) + offset
+ * (TW_PLAN_MEASURED_SPLIT); an offset whose pieces take more keeps it whole
+ * (TW_PLAN_MEASURED_OVER_WAVES), since the planner never exceeds the
+ * unsplit wave count.  A T the table does not list gets tw_split_plan's
+ * analytic plan.  The wave fields always describe the returned pieces.
+ * Errors: those of tw_split_plan; TW_ERR_INVALID_ARG also for table_len < 0,
+ * a NULL table with table_len > 0, token counts not >= 1 and strictly
+ * ascending, or an offset outside [0, floor(num_tokens/2)) other than -1.
+ */
+tw_status tw_split_plan_measured(const tw_split_problem* in, const tw_split_entry* table,
+                                 int32_t table_len, tw_split_plan_result* out);
 
 /* Static description of a status code. */
 const char* tw_status_string(tw_status s);

@@ -46,8 +46,12 @@ from .planner import (  # noqa: F401
     REASON_SINGLE_WAVE,
     REASON_NO_FEASIBLE_OFFSET,
     REASON_EMPTY,
+    REASON_MEASURED_SPLIT,
+    REASON_MEASURED_UNSPLIT,
+    REASON_MEASURED_OVER_WAVES,
     ctas,
     waves,
     simulate_waves,
     split_plan,
+    split_plan_measured,
 )

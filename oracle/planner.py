@@ -31,6 +31,12 @@ Readings where the page is silent or its example disagrees with its rule:
 * The CTA count of the GEMM is modelled as ceil(M / tokens_per_cta) times the
   number of tiles across the output features, and a wave holds
   num_cus * ctas_per_cu CTAs (the page assumes one CTA per SM).
+* A measured table (the page's per-shape lookup of the offset its offline
+  timing found fastest) is consulted after the threshold and the one-wave
+  rule, in the page's order.  Its offset is applied as half + offset, and it
+  is still held to the wave condition: an entry whose two pieces would take
+  more waves than the whole batch keeps the batch whole.  An entry of -1
+  (the sweep found the whole batch fastest) keeps it whole too.
 """
 
 from __future__ import annotations
@@ -45,6 +51,9 @@ REASON_BELOW_THRESHOLD = 1
 REASON_SINGLE_WAVE = 2
 REASON_NO_FEASIBLE_OFFSET = 3
 REASON_EMPTY = 4
+REASON_MEASURED_SPLIT = 5
+REASON_MEASURED_UNSPLIT = 6
+REASON_MEASURED_OVER_WAVES = 7
 
 
 def _ceil_div(a: int, b: int) -> int:
@@ -119,3 +128,48 @@ def split_plan(num_tokens: int, tokens_per_cta: int = 1, ctas_per_token_tile: in
                         waves_unsplit=W, waves_prefix=wp, waves_suffix=ws,
                         reason=REASON_SPLIT)
     return no_split(REASON_NO_FEASIBLE_OFFSET)
+
+
+def split_plan_measured(num_tokens: int, table, tokens_per_cta: int = 1,
+                        ctas_per_token_tile: int = 1, num_cus: int = 256, ctas_per_cu: int = 1,
+                        min_split_tokens: int = 0, offsets: Sequence[int] | None = None) -> dict:
+    """Plan the split with a measured per-shape table, as [Blog] section
+    "Fix one" keeps the offset its offline timing sweep chose for each shape.
+
+    ``table`` maps token counts to the measured offset (-1: the whole batch
+    was fastest).  The threshold and the one-wave rule come first; a count
+    with no entry gets the analytic plan of :func:`split_plan`.
+    """
+    T = num_tokens
+
+    def wv(m):
+        return waves(m, tokens_per_cta, ctas_per_token_tile, num_cus, ctas_per_cu)
+
+    for t, off in dict(table).items():
+        if t < 1 or not (off == -1 or 0 <= off < t // 2):
+            raise ValueError(f"table entry {t}: offset {off} outside [0, T/2) or -1")
+    W = wv(T)
+
+    def no_split(reason):
+        return dict(prefix_tokens=T, suffix_tokens=0, offset=-1, waves_unsplit=W,
+                    waves_prefix=W, waves_suffix=0, reason=reason)
+
+    if T == 0:
+        return no_split(REASON_EMPTY)
+    if T < min_split_tokens:
+        return no_split(REASON_BELOW_THRESHOLD)
+    if W <= 1:
+        return no_split(REASON_SINGLE_WAVE)
+    if T not in dict(table):
+        return split_plan(T, tokens_per_cta, ctas_per_token_tile, num_cus, ctas_per_cu,
+                          min_split_tokens, offsets)
+    off = dict(table)[T]
+    if off == -1:                       # the sweep kept this shape whole
+        return no_split(REASON_MEASURED_UNSPLIT)
+    prefix = T // 2 + off
+    suffix = T - prefix
+    wp, ws = wv(prefix), wv(suffix)
+    if wp + ws > W:                     # the wave condition still holds the plan
+        return no_split(REASON_MEASURED_OVER_WAVES)
+    return dict(prefix_tokens=prefix, suffix_tokens=suffix, offset=off, waves_unsplit=W,
+                waves_prefix=wp, waves_suffix=ws, reason=REASON_MEASURED_SPLIT)

@@ -8,6 +8,8 @@ The Python names mirror the C entry points:
   workgroups (the pages' few-CTA footprint),
 * :func:`tw_shard_rmsnorm` -- one rank's token shard,
 * :func:`tw_split_plan` -- the prefix/suffix split plan,
+* :func:`tw_split_plan_measured` -- the split plan with a measured per-shape
+  offset table consulted first,
 * :func:`tw_fused_reduce_rmsnorm_split` -- the two launches of a split,
 * :func:`tw_reduce_partials`, :func:`tw_add_rmsnorm` and
   :func:`tw_unfused_reduce_rmsnorm` -- the unfused comparator (a standalone
@@ -20,13 +22,13 @@ from a measured offline table (:func:`split_table_from_sweep`).
 
 from ._lib import (  # noqa: F401
     LIB_PATH,
-    PLAN_MEASURED_UNSPLIT,
     PLAN_REASONS,
     PreparedFused,
     SplitPlanCache,
     TokenWeaveError,
     declared_functions,
     load_library,
+    split_table,
     split_table_from_sweep,
     tw_fused_reduce_rmsnorm,
     tw_fused_reduce_rmsnorm_grid,
@@ -36,5 +38,6 @@ from ._lib import (  # noqa: F401
     tw_set_pointer_checks,
     tw_shard_rmsnorm,
     tw_split_plan,
+    tw_split_plan_measured,
     tw_unfused_reduce_rmsnorm,
 )

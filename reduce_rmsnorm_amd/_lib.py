@@ -28,12 +28,11 @@ TW_F32, TW_BF16 = 0, 1
 TW_MAX_PARTIALS = 16
 TW_PLAN_SPLIT, TW_PLAN_BELOW_THRESHOLD, TW_PLAN_SINGLE_WAVE = 0, 1, 2
 TW_PLAN_NO_FEASIBLE_OFFSET, TW_PLAN_EMPTY = 3, 4
-# Reason code of a plan taken from a measured table that keeps the batch
-# whole (the C planner's own codes are the TW_PLAN_* above).
-PLAN_MEASURED_UNSPLIT = 5
+TW_PLAN_MEASURED_SPLIT, TW_PLAN_MEASURED_UNSPLIT, TW_PLAN_MEASURED_OVER_WAVES = 5, 6, 7
 
 PLAN_REASONS = {0: "split", 1: "below_threshold", 2: "single_wave", 3: "no_feasible_offset",
-                4: "empty", 5: "measured_unsplit"}
+                4: "empty", 5: "measured_split", 6: "measured_unsplit",
+                7: "measured_over_waves"}
 
 
 class TokenWeaveError(RuntimeError):
@@ -48,6 +47,10 @@ class SplitProblem(ctypes.Structure):
                 ("ctas_per_token_tile", ctypes.c_int64), ("num_cus", ctypes.c_int32),
                 ("ctas_per_cu", ctypes.c_int32), ("min_split_tokens", ctypes.c_int64),
                 ("offsets", ctypes.POINTER(ctypes.c_int32)), ("num_offsets", ctypes.c_int32)]
+
+
+class SplitEntry(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int64), ("offset", ctypes.c_int32)]
 
 
 class SplitPlanResult(ctypes.Structure):
@@ -82,6 +85,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tw_add_rmsnorm.restype = ctypes.c_int
     lib.tw_split_plan.argtypes = [ctypes.POINTER(SplitProblem), ctypes.POINTER(SplitPlanResult)]
     lib.tw_split_plan.restype = ctypes.c_int
+    lib.tw_split_plan_measured.argtypes = [ctypes.POINTER(SplitProblem), ctypes.POINTER(SplitEntry),
+                                           i32, ctypes.POINTER(SplitPlanResult)]
+    lib.tw_split_plan_measured.restype = ctypes.c_int
     lib.tw_status_string.argtypes = [ctypes.c_int]
     lib.tw_status_string.restype = ctypes.c_char_p
     lib.tw_last_error.argtypes = []
@@ -275,11 +281,8 @@ def tw_unfused_reduce_rmsnorm(partials, residual: torch.Tensor, weight: torch.Te
     return out, residual_out, reduced
 
 
-def tw_split_plan(num_tokens: int, tokens_per_cta: int = 1, ctas_per_token_tile: int = 1,
-                  num_cus: int = 256, ctas_per_cu: int = 1, min_split_tokens: int = 0,
-                  offsets: Optional[Sequence[int]] = None) -> dict:
-    """Wave-aware prefix/suffix split plan (host only)."""
-    lib = load_library()
+def _split_problem(num_tokens, tokens_per_cta, ctas_per_token_tile, num_cus, ctas_per_cu,
+                   min_split_tokens, offsets):
     arr = None
     if offsets is not None:
         arr = (ctypes.c_int32 * len(offsets))(*offsets)
@@ -287,9 +290,46 @@ def tw_split_plan(num_tokens: int, tokens_per_cta: int = 1, ctas_per_token_tile:
                         min_split_tokens,
                         ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)) if arr is not None else None,
                         len(offsets) if offsets is not None else 0)
+    return prob, arr
+
+
+def _plan_dict(res: SplitPlanResult) -> dict:
+    return {f: getattr(res, f) for f, _ in SplitPlanResult._fields_}
+
+
+def tw_split_plan(num_tokens: int, tokens_per_cta: int = 1, ctas_per_token_tile: int = 1,
+                  num_cus: int = 256, ctas_per_cu: int = 1, min_split_tokens: int = 0,
+                  offsets: Optional[Sequence[int]] = None) -> dict:
+    """Wave-aware prefix/suffix split plan (host only)."""
+    lib = load_library()
+    prob, _keep = _split_problem(num_tokens, tokens_per_cta, ctas_per_token_tile, num_cus,
+                                 ctas_per_cu, min_split_tokens, offsets)
     res = SplitPlanResult()
     _check(lib.tw_split_plan(ctypes.byref(prob), ctypes.byref(res)))
-    return {f: getattr(res, f) for f, _ in SplitPlanResult._fields_}
+    return _plan_dict(res)
+
+
+def split_table(measured) -> ctypes.Array:
+    """A measured table ({token count: offset, -1 for whole}) as the C
+    planner's ascending array of tw_split_entry."""
+    items = sorted((int(t), int(off)) for t, off in dict(measured).items())
+    return (SplitEntry * len(items))(*[SplitEntry(t, off) for t, off in items])
+
+
+def tw_split_plan_measured(num_tokens: int, table, tokens_per_cta: int = 1,
+                           ctas_per_token_tile: int = 1, num_cus: int = 256,
+                           ctas_per_cu: int = 1, min_split_tokens: int = 0,
+                           offsets: Optional[Sequence[int]] = None) -> dict:
+    """The split plan with a measured per-shape table consulted first (host
+    only).  ``table`` is a {token count: offset} mapping (-1: keep whole) or
+    an array from :func:`split_table`."""
+    lib = load_library()
+    arr = table if isinstance(table, ctypes.Array) else split_table(table)
+    prob, _keep = _split_problem(num_tokens, tokens_per_cta, ctas_per_token_tile, num_cus,
+                                 ctas_per_cu, min_split_tokens, offsets)
+    res = SplitPlanResult()
+    _check(lib.tw_split_plan_measured(ctypes.byref(prob), arr, len(arr), ctypes.byref(res)))
+    return _plan_dict(res)
 
 
 def tw_fused_reduce_rmsnorm_split(partials, residual: torch.Tensor, weight: torch.Tensor,
@@ -355,18 +395,14 @@ class SplitPlanCache:
 
     ``measured`` optionally maps token counts to the offset an offline sweep
     found fastest (-1: keep the batch whole), the way the pages choose their
-    offsets by timing.  A count in it gets that split; any other count gets
-    tw_split_plan's analytic plan.  The wave fields always come from the
-    analytic planner."""
+    offsets by timing.  The table is handed to tw_split_plan_measured, which
+    applies a listed offset when its pieces meet the wave condition and plans
+    every other count analytically; this class only stores the plans."""
 
     def __init__(self, measured: Optional[dict] = None, **problem):
         self._problem = problem
-        self._measured = {}
-        for t, off in (measured or {}).items():
-            t, off = int(t), int(off)
-            if t < 1 or not (off == -1 or 0 <= off < t // 2):
-                raise ValueError(f"measured split for {t} tokens: offset {off} outside [0, T/2) or -1")
-            self._measured[t] = off
+        self._table = split_table(measured or {})
+        tw_split_plan_measured(0, self._table, **problem)    # validates table and problem
         self._plans = {}
 
     def __call__(self, num_tokens: int) -> dict:
@@ -374,17 +410,7 @@ class SplitPlanCache:
         alone)."""
         plan = self._plans.get(num_tokens)
         if plan is None:
-            plan = tw_split_plan(num_tokens, **self._problem)
-            off = self._measured.get(num_tokens)
-            if off is not None:
-                plan = dict(plan)
-                if off < 0:
-                    plan.update(prefix_tokens=num_tokens, suffix_tokens=0, offset=-1,
-                                reason=PLAN_MEASURED_UNSPLIT)
-                else:
-                    prefix = num_tokens // 2 + off
-                    plan.update(prefix_tokens=prefix, suffix_tokens=num_tokens - prefix,
-                                offset=off, reason=TW_PLAN_SPLIT)
+            plan = tw_split_plan_measured(num_tokens, self._table, **self._problem)
             self._plans[num_tokens] = plan
         return dict(plan)
 

@@ -4,7 +4,9 @@
  *
  * stdin: planner cases, one per line:
  *   num_tokens tokens_per_cta ctas_per_token_tile num_cus ctas_per_cu min_split_tokens
- * stdout: one line per case,
+ *   table_tokens table_offset
+ * stdout: one line per case, the analytic plan and then the plan with a
+ * one-entry measured table {table_tokens: table_offset}, each as
  *   status prefix suffix offset waves_unsplit waves_prefix waves_suffix reason
  * then the results of the argument checks below, one "name status" line each,
  * and "done" last.  Exit status 0 unless a check of this program's own fails.
@@ -25,8 +27,8 @@ static int report(const char* name, tw_status s) {
 
 int main(void) {
   int fail = 0;
-  long long T, tpc, tiles, thr;
-  int cus, occ;
+  long long T, tpc, tiles, thr, tab_t;
+  int cus, occ, tab_off;
   char line[256];
 
   if (tw_abi_version() != TW_ABI_VERSION) {
@@ -37,7 +39,10 @@ int main(void) {
     tw_split_problem p;
     tw_split_plan_result r;
     tw_status s;
-    if (sscanf(line, "%lld %lld %lld %d %d %lld", &T, &tpc, &tiles, &cus, &occ, &thr) != 6) continue;
+    tw_split_entry e;
+    if (sscanf(line, "%lld %lld %lld %d %d %lld %lld %d", &T, &tpc, &tiles, &cus, &occ, &thr,
+               &tab_t, &tab_off) != 8)
+      continue;
     memset(&p, 0, sizeof p);
     p.num_tokens = T;
     p.tokens_per_cta = tpc;
@@ -48,6 +53,12 @@ int main(void) {
     p.offsets = NULL; /* the default offset set */
     p.num_offsets = 0;
     s = tw_split_plan(&p, &r);
+    printf("%d %lld %lld %d %d %d %d %d ", (int)s, (long long)r.prefix_tokens,
+           (long long)r.suffix_tokens, (int)r.offset, (int)r.waves_unsplit, (int)r.waves_prefix,
+           (int)r.waves_suffix, (int)r.reason);
+    e.num_tokens = tab_t;
+    e.offset = tab_off;
+    s = tw_split_plan_measured(&p, &e, 1, &r);
     printf("%d %lld %lld %d %d %d %d %d\n", (int)s, (long long)r.prefix_tokens,
            (long long)r.suffix_tokens, (int)r.offset, (int)r.waves_unsplit, (int)r.waves_prefix,
            (int)r.waves_suffix, (int)r.reason);
@@ -86,6 +97,19 @@ int main(void) {
     p.num_cus = 256;
     p.ctas_per_cu = 1;
     fail |= report("plan_zero_tile", tw_split_plan(&p, &r));
+    {
+      tw_split_entry t[2];
+      p.tokens_per_cta = 1;
+      t[0].num_tokens = 200;
+      t[0].offset = 0;
+      t[1].num_tokens = 100;
+      t[1].offset = 0;
+      fail |= report("plan_table_not_ascending", tw_split_plan_measured(&p, t, 2, &r));
+      t[0].num_tokens = 100;
+      t[0].offset = 50;
+      fail |= report("plan_table_offset_at_half", tw_split_plan_measured(&p, t, 1, &r));
+      fail |= report("plan_table_null", tw_split_plan_measured(&p, NULL, 1, &r));
+    }
   }
   {
     /* Randomized argument sets, each invalid by construction (an output

@@ -35,7 +35,8 @@ def test_exports_every_declared_symbol(lib):
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in dyn.splitlines() if " T " in ln}
     assert set(names) <= exported
-    assert lib.tw_abi_version() == 1
+    header = open(tw.declared_functions.__defaults__[0]).read()
+    assert lib.tw_abi_version() == int(re.search(r"#define TW_ABI_VERSION (\d+)", header).group(1))
 
 
 def test_every_entry_point_has_a_python_binding():
@@ -321,31 +322,90 @@ def test_last_error_is_per_thread(lib):
 
 def test_plan_constants_match_the_header():
     text = open(os.path.join(os.path.dirname(_lib.LIB_PATH), "..", "include", "tokenweave.h")).read()
-    for name in ("TW_PLAN_SPLIT", "TW_PLAN_BELOW_THRESHOLD", "TW_PLAN_SINGLE_WAVE",
-                 "TW_PLAN_NO_FEASIBLE_OFFSET", "TW_PLAN_EMPTY"):
+    names = ("TW_PLAN_SPLIT", "TW_PLAN_BELOW_THRESHOLD", "TW_PLAN_SINGLE_WAVE",
+             "TW_PLAN_NO_FEASIBLE_OFFSET", "TW_PLAN_EMPTY", "TW_PLAN_MEASURED_SPLIT",
+             "TW_PLAN_MEASURED_UNSPLIT", "TW_PLAN_MEASURED_OVER_WAVES")
+    for name in names:
         m = re.search(rf"#define {name} (\d+)", text)
         assert m and int(m.group(1)) == getattr(_lib, name), name
         assert tw.PLAN_REASONS[getattr(_lib, name)]
-    assert tw.PLAN_MEASURED_UNSPLIT not in range(5)
+        assert getattr(oracle, "REASON" + name[len("TW_PLAN"):]) == getattr(_lib, name)
+    assert len({getattr(_lib, n) for n in names}) == len(names)
+
+
+# The offline sweep's table (fastest offset per token count, -1 for the whole
+# batch) of one Llama-3-70B-shaped layer step: 256 x 256 GEMM tiles, 32 across
+# h = 8192, 256 CUs, threshold 1024.  It lists a count whose measured offset
+# breaks the wave bound (5632 at offset 128: 2 + 2 waves against 3).
+MEASURED_SWEEP = {1024: -1, 1536: -1, 2048: -1, 2560: -1, 3072: -1, 3584: -1, 4096: -1,
+                  4608: -1, 5120: 512, 5632: 128, 6144: -1, 6656: 192, 7168: 256, 7680: 256,
+                  8192: -1}
+SWEEP_MODEL = dict(tokens_per_cta=256, ctas_per_token_tile=32, num_cus=256, ctas_per_cu=1,
+                   min_split_tokens=1024)
+
+
+def test_measured_plan_matches_the_oracle_on_the_sweep_table():
+    # Every listed count and every count between them, bit-exact in every field.
+    for T in sorted(set(MEASURED_SWEEP) | set(range(0, 8400, 64))):
+        assert tw.tw_split_plan_measured(T, MEASURED_SWEEP, **SWEEP_MODEL) == \
+            oracle.split_plan_measured(T, MEASURED_SWEEP, **SWEEP_MODEL), T
+    p = tw.tw_split_plan_measured(5632, MEASURED_SWEEP, **SWEEP_MODEL)
+    assert p["reason"] == _lib.TW_PLAN_MEASURED_OVER_WAVES and p["suffix_tokens"] == 0
+    p = tw.tw_split_plan_measured(5120, MEASURED_SWEEP, **SWEEP_MODEL)
+    assert (p["prefix_tokens"], p["suffix_tokens"], p["reason"]) == \
+        (3072, 2048, _lib.TW_PLAN_MEASURED_SPLIT)
+
+
+def test_measured_plan_matches_the_oracle_on_random_tables():
+    rng = random.Random(11)
+    for _ in range(300):
+        cus = rng.choice([7, 64, 132, 256])
+        kw = dict(tokens_per_cta=rng.choice([1, 16, 128]), ctas_per_token_tile=rng.choice([1, 3, 32]),
+                  num_cus=cus, ctas_per_cu=rng.choice([1, 2]),
+                  min_split_tokens=rng.choice([0, 100, 1024]))
+        counts = sorted(rng.sample(range(1, 5000), rng.randint(0, 12)))
+        table = {t: rng.choice([-1] + [o for o in (0, 1, 64, 100, 300, 999) if o < t // 2])
+                 for t in counts}
+        arr = tw.split_table(table)
+        for T in counts + [rng.randint(0, 5000) for _ in range(5)]:
+            assert tw.tw_split_plan_measured(T, arr, **kw) == \
+                oracle.split_plan_measured(T, table, **kw), (T, table, kw)
+
+
+def test_measured_plan_with_an_empty_table_is_the_analytic_plan():
+    for T in range(0, 700, 7):
+        assert tw.tw_split_plan_measured(T, {}, num_cus=132) == tw.tw_split_plan(T, num_cus=132)
+
+
+def test_measured_plan_rejects_bad_tables(lib):
+    for bad in ({100: 50}, {100: -2}, {0: -1}, {101: 50}):
+        with pytest.raises(tw.TokenWeaveError) as e:
+            tw.tw_split_plan_measured(100, bad)
+        assert e.value.status == INVALID
+    # not ascending, duplicated, negative length, NULL with a length
+    unsorted = (_lib.SplitEntry * 2)(_lib.SplitEntry(200, 0), _lib.SplitEntry(100, 0))
+    dup = (_lib.SplitEntry * 2)(_lib.SplitEntry(100, 0), _lib.SplitEntry(100, 1))
+    prob, _ = _lib._split_problem(100, 1, 1, 256, 1, 0, None)
+    res = _lib.SplitPlanResult()
+    for arr, n in ((unsorted, 2), (dup, 2), (dup, -1), (None, 3)):
+        assert lib.tw_split_plan_measured(ctypes.byref(prob), arr, n, ctypes.byref(res)) == INVALID
+    assert lib.tw_split_plan_measured(None, dup, 1, ctypes.byref(res)) == INVALID
+    assert lib.tw_split_plan_measured(ctypes.byref(prob), dup, 1, None) == INVALID
 
 
 def test_split_plan_cache_with_a_measured_table():
-    problem = dict(tokens_per_cta=256, ctas_per_token_tile=32, num_cus=256, min_split_tokens=1024)
+    # The cache only stores the C planner's plans: the table's split where it
+    # meets the wave bound, the whole batch where the table says so or where
+    # its offset breaks the bound, and the analytic plan elsewhere.
+    cache = tw.SplitPlanCache(measured=MEASURED_SWEEP, **SWEEP_MODEL)
+    for T in (1024, 3072, 5120, 5632, 6656, 6000, 8192, 9000):
+        assert cache(T) == oracle.split_plan_measured(T, MEASURED_SWEEP, **SWEEP_MODEL)
+    got = cache(5120)
+    got["prefix_tokens"] = 0                                           # a copy: the table keeps its plan
+    assert cache(5120)["prefix_tokens"] == 3072
     table = tw.split_table_from_sweep([{"tokens": 5632, "fastest": 128},
                                        {"tokens": 4096, "fastest": -1}])
-    cache = tw.SplitPlanCache(measured=table, **problem)
-    analytic = oracle.split_plan(5632, **problem)
-    p = cache(5632)
-    assert analytic["reason"] == oracle.REASON_NO_FEASIBLE_OFFSET      # the planner would not split
-    assert (p["prefix_tokens"], p["suffix_tokens"], p["offset"], p["reason"]) == (2944, 2688, 128, 0)
-    assert p["waves_unsplit"] == analytic["waves_unsplit"]
-    q = cache(4096)
-    assert (q["prefix_tokens"], q["suffix_tokens"], q["offset"], q["reason"]) == \
-        (4096, 0, -1, tw.PLAN_MEASURED_UNSPLIT)
-    assert cache(3072) == oracle.split_plan(3072, **problem)           # not in the table: analytic
-    got = cache(5632)
-    got["prefix_tokens"] = 0                                           # a copy: the table keeps its plan
-    assert cache(5632)["prefix_tokens"] == 2944
+    assert table == {5632: 128, 4096: -1}
     for bad in ({100: 50}, {100: -2}, {0: -1}):
-        with pytest.raises(ValueError):
-            tw.SplitPlanCache(measured=bad, **problem)
+        with pytest.raises(tw.TokenWeaveError):
+            tw.SplitPlanCache(measured=bad, **SWEEP_MODEL)

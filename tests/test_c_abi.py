@@ -1,7 +1,7 @@
 """The C ABI from plain C: tests/c/abi_check.c is compiled as C99 (and, to
 check the header's C++ guards, as C++11) against include/tokenweave.h and
-linked with the built library.  Its planner results must match the oracle
-field for field, and its argument checks must return the documented status
+linked with the built library.  Its planner results (analytic, and with a
+measured table) must match the oracle field for field, and its argument checks must return the documented status
 codes.  No device work: runs without a GPU."""
 
 import os
@@ -29,6 +29,9 @@ EXPECTED_STATUS = {
     "empty_batch": _lib.TW_OK,
     "plan_null_problem": _lib.TW_ERR_INVALID_ARG,
     "plan_zero_tile": _lib.TW_ERR_INVALID_ARG,
+    "plan_table_not_ascending": _lib.TW_ERR_INVALID_ARG,
+    "plan_table_offset_at_half": _lib.TW_ERR_INVALID_ARG,
+    "plan_table_null": _lib.TW_ERR_INVALID_ARG,
     "randomized_refused": 0,      # 0: every randomized invalid call was refused
 }
 
@@ -56,7 +59,26 @@ def cases():
     for _ in range(300):
         c.append((rnd.randint(0, 70000), rnd.choice([1, 64, 128, 256]), rnd.randint(1, 64),
                   rnd.choice([132, 256, 304]), rnd.randint(1, 4), rnd.choice([0, 1024, 4096])))
-    return c
+    # each case also carries a one-entry measured table: its own token count
+    # (with an offset that may or may not meet the wave bound), or another one
+    out = []
+    for k, case in enumerate(c):
+        T = case[0]
+        if T >= 2 and k % 3 != 2:
+            off = rnd.choice([-1] + [o for o in (0, 64, 128, 512, T // 2 - 1)
+                                     if 0 <= o < min(T // 2, 2 ** 31)])
+            out.append(case + (T, off))
+        else:
+            out.append(case + (T + 1000, -1))
+    return out
+
+
+def _want(case):
+    T, tpc, tiles, cus, occ, thr, tab_t, tab_off = case
+    kw = dict(tokens_per_cta=tpc, ctas_per_token_tile=tiles, num_cus=cus, ctas_per_cu=occ,
+              min_split_tokens=thr)
+    return ([_lib.TW_OK] + [oracle.split_plan(T, **kw)[f] for f in FIELDS] + [_lib.TW_OK] +
+            [oracle.split_plan_measured(T, {tab_t: tab_off}, **kw)[f] for f in FIELDS])
 
 
 @pytest.mark.parametrize("compiler,std,lang", [("gcc", "c99", "c"), ("g++", "c++11", "c++")])
@@ -72,12 +94,7 @@ def test_c_program_matches_oracle(tmp_path, cases, compiler, std, lang):
     lines = run.stdout.splitlines()
     assert lines[-1] == "done"
     for c, ln in zip(cases, lines[:len(cases)]):
-        got = [int(v) for v in ln.split()]
-        assert got[0] == _lib.TW_OK, (c, ln)
-        T, tpc, tiles, cus, occ, thr = c
-        want = oracle.split_plan(T, tokens_per_cta=tpc, ctas_per_token_tile=tiles, num_cus=cus,
-                                 ctas_per_cu=occ, min_split_tokens=thr)
-        assert got[1:] == [want[f] for f in FIELDS], (c, got, want)
+        assert [int(v) for v in ln.split()] == _want(c), (c, ln)
     checks = dict(ln.split() for ln in lines[len(cases):-1])
     assert {k: int(v) for k, v in checks.items()} == EXPECTED_STATUS
 
@@ -120,9 +137,6 @@ def test_c_program_under_address_and_undefined_sanitizers(tmp_path, cases):
     lines = run.stdout.splitlines()
     assert lines[-1] == "done"
     for c, ln in zip(cases, lines[:len(cases)]):
-        T, tpc, tiles, cus, occ, thr = c
-        want = oracle.split_plan(T, tokens_per_cta=tpc, ctas_per_token_tile=tiles, num_cus=cus,
-                                 ctas_per_cu=occ, min_split_tokens=thr)
-        assert [int(v) for v in ln.split()][1:] == [want[f] for f in FIELDS], (c, ln)
+        assert [int(v) for v in ln.split()] == _want(c), (c, ln)
     checks = dict(ln.split() for ln in lines[len(cases):-1])
     assert {k: int(v) for k, v in checks.items()} == EXPECTED_STATUS

@@ -134,3 +134,75 @@ def test_custom_offsets_and_tiles():
     assert (p["prefix_tokens"], p["suffix_tokens"], p["offset"], p["waves_unsplit"]) == (2048, 2048, 0, 2)
     p = oracle.split_plan(514, num_cus=256, offsets=[0, 10, 100])
     assert p["offset"] == 10 and p["prefix_tokens"] == 267
+
+
+# A per-shape table as the offline sweep of one layer step fills it (the
+# fastest offset per token count, -1 for the whole batch): the layer GEMM of a
+# Llama-3-70B-shaped rank, 256 x 256 tiles, 32 across h = 8192, 256 CUs,
+# threshold 1024.  Any table is a valid input; this one has entries of every
+# kind.
+MEASURED_SWEEP = {1024: -1, 1536: -1, 2048: -1, 2560: -1, 3072: -1, 3584: -1, 4096: -1,
+                  4608: -1, 5120: 512, 5632: 128, 6144: -1, 6656: 192, 7168: 256, 7680: 256,
+                  8192: -1}
+SWEEP_MODEL = dict(tokens_per_cta=256, ctas_per_token_tile=32, num_cus=256, ctas_per_cu=1,
+                   min_split_tokens=1024)
+
+
+# Under that model a wave is 2048 rows: waves(M) = ceil(ceil(M / 256) * 32 / 256)
+# = ceil(M / 2048).  Derived by hand: (prefix, suffix, waves_unsplit,
+# waves_prefix, waves_suffix, reason).
+@pytest.mark.parametrize("T,want", [
+    (1024, (1024, 0, 1, 1, 0, P.REASON_SINGLE_WAVE)),    # one wave: the table is not read
+    (2048, (2048, 0, 1, 1, 0, P.REASON_SINGLE_WAVE)),
+    (2560, (2560, 0, 2, 2, 0, P.REASON_MEASURED_UNSPLIT)),
+    (4608, (4608, 0, 3, 3, 0, P.REASON_MEASURED_UNSPLIT)),
+    (5120, (3072, 2048, 3, 2, 1, P.REASON_MEASURED_SPLIT)),     # 2560 + 512 | 2048
+    (5632, (5632, 0, 3, 3, 0, P.REASON_MEASURED_OVER_WAVES)),   # 2944 | 2688: 2 + 2 > 3
+    (6656, (3520, 3136, 4, 2, 2, P.REASON_MEASURED_SPLIT)),
+    (7168, (3840, 3328, 4, 2, 2, P.REASON_MEASURED_SPLIT)),
+    (7680, (4096, 3584, 4, 2, 2, P.REASON_MEASURED_SPLIT)),
+    (8192, (8192, 0, 4, 4, 0, P.REASON_MEASURED_UNSPLIT)),
+])
+def test_measured_table_hand_derived(T, want):
+    p = oracle.split_plan_measured(T, MEASURED_SWEEP, **SWEEP_MODEL)
+    got = (p["prefix_tokens"], p["suffix_tokens"], p["waves_unsplit"], p["waves_prefix"],
+           p["waves_suffix"], p["reason"])
+    assert got == want
+    assert p["offset"] == (MEASURED_SWEEP[T] if p["suffix_tokens"] else -1)
+
+
+def test_measured_table_properties():
+    # Counts not in the table get the analytic plan; every plan keeps every
+    # token and never takes more waves than the whole batch, with the wave
+    # counts re-derived by the brute-force scheduler.
+    S = SWEEP_MODEL["num_cus"]
+    for T in list(range(0, 9000, 128)) + list(MEASURED_SWEEP):
+        p = oracle.split_plan_measured(T, MEASURED_SWEEP, **SWEEP_MODEL)
+        if T not in MEASURED_SWEEP:
+            assert p == oracle.split_plan(T, **SWEEP_MODEL)
+        assert p["prefix_tokens"] + p["suffix_tokens"] == T
+        ctas = [oracle.ctas(m, 256, 32) for m in (T, p["prefix_tokens"], p["suffix_tokens"])]
+        assert [oracle.simulate_waves(c, S) for c in ctas] == \
+            [p["waves_unsplit"], p["waves_prefix"], p["waves_suffix"]]
+        assert p["waves_prefix"] + p["waves_suffix"] <= p["waves_unsplit"]
+        if p["suffix_tokens"]:
+            assert p["prefix_tokens"] == T // 2 + p["offset"]
+
+
+def test_measured_table_of_the_analytic_choices_gives_the_analytic_splits():
+    for T in range(1, 601):
+        a = oracle.split_plan(T, num_cus=132)
+        table = {T: a["offset"]} if a["reason"] == P.REASON_SPLIT else {}
+        m = oracle.split_plan_measured(T, table, num_cus=132)
+        fields = ("prefix_tokens", "suffix_tokens", "offset", "waves_unsplit", "waves_prefix",
+                  "waves_suffix")
+        assert [m[f] for f in fields] == [a[f] for f in fields]
+        assert m["reason"] == (P.REASON_MEASURED_SPLIT if table else a["reason"])
+
+
+def test_measured_table_rejects_offsets_outside_half():
+    for bad in ({100: 50}, {100: -2}, {0: 0}, {101: 50}):
+        with pytest.raises(ValueError):
+            oracle.split_plan_measured(100, bad)
+    # 101 tokens: half = 50, so 49 is the largest offset
+    assert oracle.split_plan_measured(101, {101: 49}, num_cus=1)["prefix_tokens"] == 99
