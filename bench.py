@@ -46,8 +46,10 @@ METRIC = "fused reduce-add-RMSNorm HBM GB/s (% of peak), h=8192 T=1024 N=8 bf16"
 # From a pause, the GPU needs about 30 ms of sustained load before launches
 # reach their steady time (its power management ramps up the clocks): the first
 # ~1000 fused launches of the 1024-row workload take 31-33 us each, the rest
-# 30.8 us (bench.py --ramp).  The default warm-up runs about three times that.
-WARMUP_SECONDS = 0.1
+# 30.8 us (bench.py --ramp).  Before the requested warm-up steps the bench
+# therefore always settles the GPU with about three times that much work.
+SETTLE_SECONDS = 0.1
+DEFAULT_WARMUP = 20
 RAMP_BLOCKS, RAMP_BLOCK = 60, 100
 EMPTY_LAUNCHES = 200
 
@@ -64,10 +66,11 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed warm-up steps (default: enough for about %.0f ms of work, so "
-                         "the GPU has settled under load before the timed steps)"
-                         % (1e3 * WARMUP_SECONDS))
+    ap.add_argument("--warmup", type=int, default=DEFAULT_WARMUP,
+                    help="untimed warm-up steps, run after a settle of about %.0f ms of the "
+                         "same steps (which always runs, so that the GPU has reached its "
+                         "steady speed under load before the timed steps)"
+                         % (1e3 * SETTLE_SECONDS))
     ap.add_argument("--ramp", action="store_true",
                     help="also time the first %d steps after a short pause, in blocks of %d: "
                          "the ramp that the warm-up covers" % (RAMP_BLOCKS * RAMP_BLOCK,
@@ -154,11 +157,15 @@ def run_ramp(torch, step, stream) -> dict:
             "steps_to_settle": settled * RAMP_BLOCK, "ms_to_settle": round(ms_to_settle, 2)}
 
 
-def run_ceiling(sets, R, rows, h, itemsize, stream, steps, timer):
+def run_ceiling(tw, sets, R, rows, h, itemsize, stream, steps, timer):
     """Time the measurement-only probes of libtw_bwprobe.so over the bench's
     own rotated buffers: sources are the partial rows and the residual rows,
-    destinations are out and residual_out."""
+    destinations are out and residual_out.  Flat streams of the same bytes
+    (reads and writes, reads only, writes only), and, where the row class has
+    one, the schedule twins of the fused launch: its geometry, load order,
+    pause, stores and row barrier without its arithmetic."""
     import ctypes
+    import torch
     lib = _probe_lib()
     tensor_bytes = rows * h * itemsize
     nvec = tensor_bytes // 16
@@ -183,6 +190,27 @@ def run_ceiling(sets, R, rows, h, itemsize, stream, steps, timer):
         res[key + "_gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
         print(f"[bench] probe {key}: {nbytes} B in {us:.2f} us = {res[key + '_gbs']} GB/s",
               file=sys.stderr, flush=True)
+    row_vecs = h * itemsize // 16
+    info = tw.tw_fused_launch_info(nsrc - 1, rows, h,
+                                   torch.bfloat16 if itemsize == 2 else torch.float32, stream)
+    if row_vecs in (512, 1024, 2048) and info["vectors_per_thread"] * \
+            info["threads_per_workgroup"] == row_vecs:
+        seq = 1 if info["kernel_name"] != "all" else 0
+        res["twin_load_order"] = "sequenced" if seq else "all at once"
+        for kind, key, nbytes in ((5, "twin_read_write", (nsrc + 2) * tensor_bytes),
+                                  (6, "twin_read_only", nsrc * tensor_bytes)):
+            def go(i, kind=kind):
+                src, n, dst = ptrs[i % R]
+                rc = lib.tw_probe_twin_launch(kind, seq, src, n, dst, nvec, rows,
+                                              stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"twin probe launch failed: {rc}")
+            us = timer(go, steps)
+            res[key + "_us"] = round(us, 3)
+            res[key + "_bytes"] = nbytes
+            res[key + "_gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+            print(f"[bench] schedule twin {key} ({res['twin_load_order']}): {nbytes} B in "
+                  f"{us:.2f} us = {res[key + '_gbs']} GB/s", file=sys.stderr, flush=True)
     return res
 
 
@@ -407,6 +435,10 @@ def _probe_lib():
                                     ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int64,
                                     ctypes.c_int, ctypes.c_void_p]
     lib.tw_probe_launch.restype = ctypes.c_int
+    lib.tw_probe_twin_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
+                                         ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
+                                         ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.tw_probe_twin_launch.restype = ctypes.c_int
     return lib
 
 
@@ -697,14 +729,19 @@ def main():
     ramp = None
     if args.ramp:
         ramp = run_ramp(torch, step, stream)
-    if args.warmup is None:
-        # Estimated step time: the bytes at 6 TB/s plus 3 us per launch.
-        est = step_bytes / 6.0e12 + 3e-6 * len(launches_per_set[0])
-        args.warmup = max(50, math.ceil(WARMUP_SECONDS / est))
-
+    # The settle: steps enough for about SETTLE_SECONDS of GPU work (estimated
+    # at the bytes at 6 TB/s plus 3 us per launch), then the requested warm-up.
+    est = step_bytes / 6.0e12 + 3e-6 * len(launches_per_set[0])
+    settle_steps = max(50, math.ceil(SETTLE_SECONDS / est))
     print(f"[bench] workload={wl.name} mode={args.mode} rows={rows} h={h} N={N} {wl.dtype} "
-          f"rotate={R} warmup={args.warmup} steps={args.steps} "
+          f"rotate={R} settle={settle_steps} warmup={args.warmup} steps={args.steps} "
           f"{'graph' if args.graph else 'eager'}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    for i in range(settle_steps):
+        step(i)
+    torch.cuda.synchronize()
+    settle = {"steps": settle_steps, "seconds": round(time.perf_counter() - t_settle, 4)}
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -854,7 +891,8 @@ def main():
 
     ceiling = None
     if args.ceiling:
-        ceiling = run_ceiling(sets, R, rows, h, wl.itemsize, stream, min(args.steps, 500), timer)
+        ceiling = run_ceiling(tw, sets, R, rows, h, wl.itemsize, stream, min(args.steps, 500),
+                              timer)
     launch_floor = None
     if args.launch_floor:
         launch_floor = run_launch_floor(torch, timer)
@@ -874,13 +912,14 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": settle,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: T={T} h={h} N={N} bf16 storage, "
+        "config": {"workload": f"{wl.name}: T={T} h={h} N={N} {wl.dtype} storage, "
                                f"{args.mode} mode ({rows} rows), eps={wl.eps}",
                    "num_tokens": T, "hidden": h, "num_partials": N, "storage_dtype": wl.dtype,
                    "mode": args.mode, "rows": rows, "rotated_input_sets": R,
@@ -915,6 +954,8 @@ def main():
         # Secondary context: the fused step against a plain stream that moves
         # exactly its bytes on the same buffers in the same run.
         ceiling["fused_over_read_write_probe"] = round(result["value"] / ceiling["read_write_gbs"], 4)
+        if "twin_read_write_gbs" in ceiling:
+            ceiling["fused_over_twin"] = round(result["value"] / ceiling["twin_read_write_gbs"], 4)
         result["ceiling"] = ceiling
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -293,6 +293,38 @@ typedef struct {
 tw_status tw_split_plan_measured(const tw_split_problem* in, const tw_split_entry* table,
                                  int32_t table_len, tw_split_plan_result* out);
 
+/*
+ * tw_fused_launch_info -- how tw_fused_reduce_rmsnorm would launch a call
+ * (host only; runtime queries, no launch).  A round is the workgroups
+ * resident at once on the CUs the stream may use: the device's CU count, or
+ * the CUs of the stream's CU mask when fewer.  The launch rules (which kernel
+ * a dispatch runs) depend on the row count against that round; they never
+ * change a result bit.  A long call is cut into dispatches of consecutive
+ * rows, each taking its own kernel for its row count; `kernel` is that of
+ * the first dispatch (of rows_per_dispatch rows).
+ *   num_partials, num_tokens, hidden, dtype, stream: as for
+ *                 tw_fused_reduce_rmsnorm (a shard or split launch passes its
+ *                 own row count)
+ *   out           non-NULL (else TW_ERR_INVALID_ARG)
+ * Errors: those of tw_fused_reduce_rmsnorm that apply to the scalars.
+ */
+#define TW_KERNEL_ALL_AT_ONCE 0   /* one workgroup per row, all loads issued at once */
+#define TW_KERNEL_SEQUENCED 1     /* one workgroup per row, tensors loaded in sequence */
+#define TW_KERNEL_STRIDED 2       /* one round of workgroups, each taking every round-th row */
+#define TW_KERNEL_BOTH_SLOTS 3    /* one workgroup per row, both vector slots' loads at once */
+typedef struct {
+  int32_t num_cus;                /* CUs counted for the stream */
+  int32_t threads_per_workgroup;
+  int32_t vectors_per_thread;     /* 16-byte vectors of a row per thread */
+  int32_t kernel;                 /* TW_KERNEL_* of the first dispatch; -1 when T == 0 */
+  int64_t round_rows;             /* workgroups resident at once */
+  int64_t rows_per_dispatch;      /* 0 when T == 0 */
+  int64_t dispatches;             /* 0 when T == 0 */
+} tw_launch_info;
+
+tw_status tw_fused_launch_info(int32_t num_partials, int64_t num_tokens, int64_t hidden,
+                               tw_dtype dtype, void* stream, tw_launch_info* out);
+
 /* Static description of a status code. */
 const char* tw_status_string(tw_status s);
 

@@ -7,6 +7,8 @@ The Python names mirror the C entry points:
 * :func:`tw_fused_reduce_rmsnorm_grid` -- every row on a fixed number of
   workgroups (the pages' few-CTA footprint),
 * :func:`tw_shard_rmsnorm` -- one rank's token shard,
+* :func:`tw_fused_launch_info` -- how a fused call would be launched (the
+  geometry, the round of resident workgroups on the stream's CUs, the kernel),
 * :func:`tw_split_plan` -- the prefix/suffix split plan,
 * :func:`tw_split_plan_measured` -- the split plan with a measured per-shape
   offset table consulted first,
@@ -32,6 +34,7 @@ from ._lib import (  # noqa: F401
     split_table_from_sweep,
     tw_fused_reduce_rmsnorm,
     tw_fused_reduce_rmsnorm_grid,
+    tw_fused_launch_info,
     tw_add_rmsnorm,
     tw_fused_reduce_rmsnorm_split,
     tw_reduce_partials,

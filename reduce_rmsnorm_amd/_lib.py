@@ -49,6 +49,17 @@ class SplitProblem(ctypes.Structure):
                 ("offsets", ctypes.POINTER(ctypes.c_int32)), ("num_offsets", ctypes.c_int32)]
 
 
+class LaunchInfo(ctypes.Structure):
+    _fields_ = [("num_cus", ctypes.c_int32), ("threads_per_workgroup", ctypes.c_int32),
+                ("vectors_per_thread", ctypes.c_int32), ("kernel", ctypes.c_int32),
+                ("round_rows", ctypes.c_int64), ("rows_per_dispatch", ctypes.c_int64),
+                ("dispatches", ctypes.c_int64)]
+
+
+TW_KERNEL_ALL_AT_ONCE, TW_KERNEL_SEQUENCED, TW_KERNEL_STRIDED, TW_KERNEL_BOTH_SLOTS = 0, 1, 2, 3
+KERNEL_NAMES = {-1: "none", 0: "all", 1: "seq", 2: "strided", 3: "both"}
+
+
 class SplitEntry(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int64), ("offset", ctypes.c_int32)]
 
@@ -88,6 +99,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tw_split_plan_measured.argtypes = [ctypes.POINTER(SplitProblem), ctypes.POINTER(SplitEntry),
                                            i32, ctypes.POINTER(SplitPlanResult)]
     lib.tw_split_plan_measured.restype = ctypes.c_int
+    lib.tw_fused_launch_info.argtypes = [i32, i64, i64, ctypes.c_int, vp,
+                                         ctypes.POINTER(LaunchInfo)]
+    lib.tw_fused_launch_info.restype = ctypes.c_int
     lib.tw_status_string.argtypes = [ctypes.c_int]
     lib.tw_status_string.restype = ctypes.c_char_p
     lib.tw_last_error.argtypes = []
@@ -224,6 +238,27 @@ def tw_shard_rmsnorm(partials, residual: torch.Tensor, weight: torch.Tensor, eps
                                     _dtype_code(residual), int(shard_index),
                                     _stream_handle(residual.device, stream)))
     return out, residual_out
+
+
+def tw_fused_launch_info(num_partials: int, num_tokens: int, hidden: int,
+                         dtype: torch.dtype = torch.bfloat16,
+                         stream: Optional[torch.cuda.Stream] = None) -> dict:
+    """How tw_fused_reduce_rmsnorm would launch a call of this shape on
+    ``stream`` (host only): the CUs counted for the stream, the geometry, the
+    round of resident workgroups, the dispatches and the first dispatch's
+    kernel ("all", "seq", "strided" or "both" in ``kernel_name``).  Without a GPU (or
+    with ``stream=None``) the stream is the null stream."""
+    lib = load_library()
+    code = TW_BF16 if dtype == torch.bfloat16 else TW_F32 if dtype == torch.float32 else None
+    if code is None:
+        raise ValueError(f"unsupported dtype {dtype}")
+    handle = ctypes.c_void_p(stream.cuda_stream) if stream is not None else None
+    info = LaunchInfo()
+    _check(lib.tw_fused_launch_info(num_partials, num_tokens, hidden, code, handle,
+                                    ctypes.byref(info)))
+    d = {f: getattr(info, f) for f, _ in LaunchInfo._fields_}
+    d["kernel_name"] = KERNEL_NAMES[d["kernel"]]
+    return d
 
 
 def tw_reduce_partials(partials, reduced: Optional[torch.Tensor] = None,

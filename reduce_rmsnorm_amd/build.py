@@ -90,7 +90,8 @@ def build(verbose: bool = False) -> str:
         for c in cmds:
             print(" ".join(c))
     probe_obj = os.path.join(BUILD, PROBE_SOURCE + ".o")
-    cmds.append([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, PROBE_SOURCE), "-o", probe_obj])
+    cmds.append([hipcc, *HIP_FLAGS, "-I", CSRC, "-c", os.path.join(CSRC, PROBE_SOURCE), "-o",
+                 probe_obj])
     if verbose:
         print(" ".join(cmds[-1]))
     _run_all(cmds)

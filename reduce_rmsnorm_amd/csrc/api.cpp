@@ -29,6 +29,54 @@ namespace {
 
 std::atomic<int> g_pointer_checks{0};
 
+// CUs of each device, queried once (0: not yet known).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_cus[kMaxDevices];
+// Used when the runtime cannot say (an MI355X has 256).
+constexpr int kFallbackCUs = 256;
+// 32-bit words of a stream's CU mask that are read: up to 1024 CUs.
+constexpr uint32_t kMaskWords = 32;
+
+int device_cus(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return 0;
+  int n = g_device_cus[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  g_device_cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// The CUs the launches of `stream` may use, which size a round of resident
+// workgroups in the launch rules: the device's CU count, or the number of
+// CUs in the stream's CU mask when that is smaller (a stream made with
+// hipExtStreamCreateWithCUMask).  Runtime queries only, no launch.
+int stream_cus(void* stream) {
+  int dev = -1;
+  const hipError_t e = stream != nullptr
+                           ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
+                           : hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return kFallbackCUs;
+  }
+  int n = device_cus(dev);
+  if (n < 1) return kFallbackCUs;
+  if (stream != nullptr) {
+    uint32_t mask[kMaskWords] = {};
+    if (hipExtStreamGetCUMask(static_cast<hipStream_t>(stream), kMaskWords, mask) == hipSuccess) {
+      int bits = 0;
+      for (uint32_t w = 0; w < kMaskWords; ++w) bits += __builtin_popcount(mask[w]);
+      if (bits > 0 && bits < n) n = bits;
+    } else {
+      (void)hipGetLastError();
+    }
+  }
+  return n;
+}
+
 // With pointer checks on: is [p, p + bytes) device memory inside one
 // allocation?  Uses runtime queries only (no launch); clears the runtime's
 // last error when a query fails.
@@ -206,6 +254,7 @@ tw_status launch_rows(const void* const* partials, int32_t n, const void* residu
   L.dtype = (int32_t)dtype;
   L.stream = stream;
   L.max_workgroups = max_workgroups;
+  L.num_cus = stream_cus(stream);
   char msg[256];
   if (launch_fused(L, msg, sizeof(msg)) != 0) {
     set_error("%s", msg);
@@ -300,6 +349,7 @@ tw_status tw_reduce_partials(const void* const* partials, int32_t num_partials, 
   L.hidden = hidden;
   L.dtype = (int32_t)dtype;
   L.stream = stream;
+  L.num_cus = tw::stream_cus(stream);
   char msg[256];
   if (tw::launch_reduce(L, msg, sizeof(msg)) != 0) {
     tw::set_error("%s", msg);
@@ -331,6 +381,37 @@ tw_status tw_add_rmsnorm(const void* input, const void* residual, const void* we
     tw::set_error("%s", msg);
     return TW_ERR_DEVICE;
   }
+  return TW_OK;
+}
+
+tw_status tw_fused_launch_info(int32_t num_partials, int64_t num_tokens, int64_t hidden,
+                               tw_dtype dtype, void* stream, tw_launch_info* out) {
+  const char* who = "tw_fused_launch_info";
+  if (out == nullptr) {
+    tw::set_error("%s: NULL result pointer", who);
+    return TW_ERR_INVALID_ARG;
+  }
+  int64_t es = 0;
+  const tw_status s = tw::check_scalars(num_partials, num_tokens, hidden, 0.0f, dtype, who, &es);
+  if (s != TW_OK) return s;
+  tw_launch_info r{};
+  r.num_cus = tw::stream_cus(stream);
+  const tw::FusedPlan p = tw::plan_fused(hidden * es / 16, num_partials, num_tokens, r.num_cus);
+  r.threads_per_workgroup = tw::fused_geometry(p.geometry, num_partials).block;
+  r.vectors_per_thread = tw::fused_geometry(p.geometry, num_partials).vpt;
+  r.round_rows = tw::round_rows(r.threads_per_workgroup, r.num_cus);
+  r.rows_per_dispatch = p.rows_per_dispatch;
+  r.dispatches = p.dispatches;
+  r.kernel = -1;
+  if (num_tokens > 0) {
+    const tw::RowKernel rk = tw::fused_row_kernel(p.geometry, num_partials, p.rows_per_dispatch,
+                                                  r.num_cus);
+    r.kernel = rk == tw::RowKernel::kStrided     ? TW_KERNEL_STRIDED
+               : rk == tw::RowKernel::kSequenced ? TW_KERNEL_SEQUENCED
+               : rk == tw::RowKernel::kBothSlots ? TW_KERNEL_BOTH_SLOTS
+                                                 : TW_KERNEL_ALL_AT_ONCE;
+  }
+  *out = r;
   return TW_OK;
 }
 

@@ -14,12 +14,23 @@
 // as the hardware reports them), which shows how a stream's CU mask maps onto
 // the eight XCDs.  A fourth does nothing at all: back-to-back launches of it
 // measure the fixed cost of a dependent launch of a given grid.
+//
+// The schedule twins bound the fused kernel's own schedule rather than a flat
+// stream: one workgroup per row of the fused kernel's geometry (geometry.h),
+// its load order (the N+1 tensors in summation order, one in flight per
+// thread, with the same pause between tensors, or all at once), its
+// non-temporal stores of both outputs and its one LDS barrier per row, with
+// the arithmetic replaced by an xor.  What a twin gains over the fused kernel
+// is what the arithmetic costs; what it lacks against the peak is the
+// schedule's own bound.
 
 #include <hip/hip_runtime.h>
 
 #include <array>
 #include <cstdint>
 #include <utility>
+
+#include "geometry.h"
 
 namespace {
 
@@ -104,7 +115,90 @@ __global__ __launch_bounds__(kPlacementBlock) void probe_placement(ProbeArgs a) 
   }
 }
 
+// Schedule twin of the fused kernel for rows of BLOCK * VPT vectors and NSRC
+// = N + 1 tensors: vector slot j of a thread is tid + j * BLOCK, the slots are
+// taken one at a time, and each slot's tensors are loaded in order with one
+// in flight (SEQ) and a pause of PACE * 64 clocks after each, or all at once
+// (!SEQ).  WRITES: both outputs are stored (residual_out per slot, out after
+// the barrier); otherwise the loads are kept alive by a store that never
+// happens for real data.
+template <int NSRC, int BLOCK, int VPT, bool SEQ, int PACE, bool WRITES>
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8)))
+void probe_row_twin(ProbeArgs a) {
+  constexpr int NW = BLOCK / 64;
+  __shared__ unsigned part[NW];
+  const int tid = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * (BLOCK * VPT);
+  u32x4 acc[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int64_t v = base + tid + j * BLOCK;
+    if constexpr (SEQ) {
+      u32x4 raw = __builtin_nontemporal_load(a.src[0] + v);
+#pragma unroll
+      for (int i = 0; i < NSRC; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        acc[j] = i == 0 ? raw : acc[j] ^ raw;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PACE > 0) __builtin_amdgcn_s_sleep(PACE);
+        if (i + 1 < NSRC) raw = __builtin_nontemporal_load(a.src[i + 1 < NSRC ? i + 1 : 0] + v);
+      }
+    } else {
+      u32x4 raw[NSRC];
+#pragma unroll
+      for (int i = 0; i < NSRC; ++i) raw[i] = __builtin_nontemporal_load(a.src[i] + v);
+      acc[j] = raw[0];
+#pragma unroll
+      for (int i = 1; i < NSRC; ++i) acc[j] ^= raw[i];
+    }
+    if constexpr (WRITES) __builtin_nontemporal_store(acc[j], a.dst[1] + v);
+  }
+  unsigned x = 0;
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) x ^= acc[j].x;
+  if ((tid & 63) == 0) part[tid >> 6] = x;
+  __syncthreads();
+  unsigned tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) tot += part[w];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int64_t v = base + tid + j * BLOCK;
+    const u32x4 o = acc[j] + tot;
+    if constexpr (WRITES) __builtin_nontemporal_store(o, a.dst[0] + v);
+    else if (o.x == 0x7F7F1234u && o.y == 0x00001234u && o.z == 0x5A5A5A5Au) a.dst[0][v] = o;
+  }
+}
+
 using ProbeFn = void (*)(ProbeArgs);
+
+// Twins for the fused kernel's sequenced row classes, by N: 1024 x 1 (rows
+// of 1024 vectors, h = 8192 bf16), 512 x 1 (512 vectors, h = 4096) and 1024 x
+// 2 (2048 vectors, h = 16384), each with the pace the fused kernel uses for
+// that class and N, and all-at-once forms for launches under one round.
+constexpr int kTwinClass[3] = {1024, 512, 2048};    // vectors per row
+constexpr int twin_pace(int c, int n) {
+  return tw::fused_pace(tw::geometry_index(kTwinClass[c]), n);
+}
+template <int C> struct TwinShape;
+template <> struct TwinShape<0> { static constexpr int block = 1024, vpt = 1; };
+template <> struct TwinShape<1> { static constexpr int block = 512, vpt = 1; };
+template <> struct TwinShape<2> { static constexpr int block = 1024, vpt = 2; };
+template <int C, bool SEQ, bool WRITES, int... Ns>
+constexpr std::array<ProbeFn, sizeof...(Ns)> twin_row(std::integer_sequence<int, Ns...>) {
+  return {&probe_row_twin<Ns + 2, TwinShape<C>::block, TwinShape<C>::vpt, SEQ,
+                          SEQ ? twin_pace(C, Ns + 1) : 0, WRITES>...};
+}
+template <bool SEQ, bool WRITES>
+constexpr std::array<std::array<ProbeFn, 16>, 3> twin_table() {
+  return {twin_row<0, SEQ, WRITES>(std::make_integer_sequence<int, 16>{}),
+          twin_row<1, SEQ, WRITES>(std::make_integer_sequence<int, 16>{}),
+          twin_row<2, SEQ, WRITES>(std::make_integer_sequence<int, 16>{})};
+}
+// [sequenced][writes][class][N - 1]
+const std::array<std::array<std::array<std::array<ProbeFn, 16>, 3>, 2>, 2> kTwin = {
+    {{twin_table<false, false>(), twin_table<false, true>()},
+     {twin_table<true, false>(), twin_table<true, true>()}}};
 
 template <int... Ks>
 constexpr std::array<ProbeFn, sizeof...(Ks)> rw_table(std::integer_sequence<int, Ks...>) {
@@ -126,9 +220,41 @@ __global__ __launch_bounds__(kEmptyBlock) void probe_empty(ProbeArgs) {}
 
 // kind 0: read+write, 1: read only, 2: write only, 3: placement (one 16-byte
 // record per workgroup into dst[0], which must hold at least grid vectors),
-// 4: empty (grid workgroups of 1024 threads; no tensor is touched).
+// 4: empty (grid workgroups of 1024 threads; no tensor is touched),
+// 5: schedule twin reading nsrc tensors and writing dst[0] (out) and dst[1]
+// (residual_out), 6: the same twin without the writes (dst[0] must still be
+// given).  The twins take grid rows of nvec / grid vectors each, which must be
+// 1024, 512 or 2048; `sequenced` selects the fused kernel's sequenced load
+// order (else all loads at once).
 // Returns 0 or a HIP error code; -1 for arguments out of range.  nvec counts
 // 16-byte vectors per tensor.
+extern "C" int tw_probe_twin_launch(int kind, int sequenced, const void* const* src, int nsrc,
+                                    void* const* dst, int64_t nvec, int grid, void* stream) {
+  if ((kind != 5 && kind != 6) || nsrc < 2 || nsrc > kMaxStreams || grid < 1 || nvec < 1 ||
+      nvec % grid != 0 || dst == nullptr || dst[0] == nullptr || (kind == 5 && dst[1] == nullptr))
+    return -1;
+  const int64_t row = nvec / grid;
+  int c = -1;
+  for (int k = 0; k < 3; ++k)
+    if (row == kTwinClass[k]) c = k;
+  if (c < 0) return -1;
+  ProbeArgs a{};
+  for (int k = 0; k < nsrc; ++k) {
+    if (src[k] == nullptr) return -1;
+    a.src[k] = static_cast<const u32x4*>(src[k]);
+  }
+  a.dst[0] = static_cast<u32x4*>(dst[0]);
+  a.dst[1] = kind == 5 ? static_cast<u32x4*>(dst[1]) : nullptr;
+  a.nsrc = nsrc;
+  a.ndst = kind == 5 ? 2 : 1;
+  a.nvec = nvec;
+  void* args[] = {&a};
+  const ProbeFn fn = kTwin[sequenced != 0][kind == 5][c][nsrc - 2];
+  const int block = c == 1 ? 512 : 1024;
+  return (int)hipLaunchKernel((const void*)fn, dim3(grid), dim3(block), args, 0,
+                              static_cast<hipStream_t>(stream));
+}
+
 extern "C" int tw_probe_launch(int kind, const void* const* src, int nsrc, void* const* dst,
                                int ndst, int64_t nvec, int grid, void* stream) {
   if (kind < 0 || kind > 4 || nsrc < 0 || nsrc > kMaxStreams || ndst < 0 || ndst > kMaxStreams ||

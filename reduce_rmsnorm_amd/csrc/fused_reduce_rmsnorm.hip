@@ -286,8 +286,8 @@ void fused_reduce_rmsnorm_kernel(const u32x4* k_first, int64_t k_row_begin, int3
 // barrier and the `out` stores overlap that row's first loads.  With one
 // workgroup per row, the rows past the last full round start on whichever
 // CUs free up first; here the workgroups that carry them were placed with
-// the first round.  Measured, that is faster when the last round is at most
-// half full (the launch rule and its figures are in geometry.h).  The per-row
+// the first round.  That is faster when the last round is at most half full
+// (the launch rule is use_strided_grid in geometry.h).  The per-row
 // arithmetic is the one-row kernel's (the same macros), so a row gives the
 // same bits in either kernel.  Two LDS buffers for the wave sums, used alternately,
 // make one barrier per row enough: a wave can only write a buffer again after
@@ -388,11 +388,14 @@ constexpr int load_order(int g, int n, bool seq_order) {
 constexpr int load_pace(int g, int n, bool seq_order) {
   return seq_order && load_order(g, n, seq_order) > 0 ? fused_pace(g, n) : 0;
 }
+constexpr int load_waves_per_eu(int g, int n, bool seq_order) {
+  return seq_order ? fused_geometry(g, n).waves_per_eu : short_form_waves_per_eu(g, n);
+}
 template <bool BF16, bool SEQ_ORDER, int G, int... Ns>
 constexpr std::array<KernelFn, sizeof...(Ns)> row_of(std::integer_sequence<int, Ns...>) {
   return {&fused_reduce_rmsnorm_kernel<Ns + 1, fused_geometry(G, Ns + 1).block,
                                        fused_geometry(G, Ns + 1).vpt, BF16,
-                                       fused_geometry(G, Ns + 1).waves_per_eu,
+                                       load_waves_per_eu(G, Ns + 1, SEQ_ORDER),
                                        fused_geometry(G, Ns + 1).chunk,
                                        load_order(G, Ns + 1, SEQ_ORDER),
                                        load_pace(G, Ns + 1, SEQ_ORDER)>...};
@@ -419,6 +422,25 @@ template <bool BF16, int... Gs>
 constexpr std::array<std::array<KernelFn, kMaxPartials>, sizeof...(Gs)> strided_table_of(
     std::integer_sequence<int, Gs...>) {
   return {strided_row_of<BF16, Gs>(std::make_integer_sequence<int, kMaxPartials>{})...};
+}
+// Both vector slots of a 1024 x 2 row loaded at once, no occupancy cap (the
+// use_both_slots rule); the same thread mapping and arithmetic as the
+// geometry's other forms.
+template <bool BF16, int G, int NN>
+constexpr KernelFn both_slots_fn() {
+  if constexpr (fused_geometry(G, NN).block == 1024 && fused_geometry(G, NN).vpt == 2 && NN <= 11)
+    return &fused_reduce_rmsnorm_kernel<NN, 1024, 2, BF16, 1, 2, 0, 0>;
+  else
+    return nullptr;
+}
+template <bool BF16, int G, int... Ns>
+constexpr std::array<KernelFn, sizeof...(Ns)> both_slots_row_of(std::integer_sequence<int, Ns...>) {
+  return {both_slots_fn<BF16, G, Ns + 1>()...};
+}
+template <bool BF16, int... Gs>
+constexpr std::array<std::array<KernelFn, kMaxPartials>, sizeof...(Gs)> both_slots_table_of(
+    std::integer_sequence<int, Gs...>) {
+  return {both_slots_row_of<BF16, Gs>(std::make_integer_sequence<int, kMaxPartials>{})...};
 }
 template <bool BF16, bool SEQ_ORDER, int G, int... Ns>
 constexpr std::array<RowsKernelFn, sizeof...(Ns)> rows_row_of(std::integer_sequence<int, Ns...>) {
@@ -448,6 +470,9 @@ const std::array<std::array<std::array<std::array<KernelFn, kMaxPartials>, kNumG
 // [bf16]
 const std::array<std::array<std::array<KernelFn, kMaxPartials>, kNumGeometries>, 2> kStridedTable = {
     {strided_table_of<false>(Geoms{}), strided_table_of<true>(Geoms{})}};
+// [bf16]
+const std::array<std::array<std::array<KernelFn, kMaxPartials>, kNumGeometries>, 2> kBothSlotsTable = {
+    {both_slots_table_of<false>(Geoms{}), both_slots_table_of<true>(Geoms{})}};
 const std::array<std::array<std::array<std::array<RowsKernelFn, kMaxPartials>, kNumGeometries>, 2>, 2>
     kRowsTable = {{{rows_table_of<false, false>(Geoms{}), rows_table_of<false, true>(Geoms{})},
                    {rows_table_of<true, false>(Geoms{}), rows_table_of<true, true>(Geoms{})}}};
@@ -466,9 +491,10 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
   const bool bf16 = L.dtype == 1;
   const int elem_bytes = bf16 ? 2 : 4;
   const int64_t nvec = L.hidden * elem_bytes / 16;
-  const int g = geometry_index(nvec);
-  if (g < 0 || nvec > kMaxVectors || L.num_partials < 1 || L.num_partials > kMaxPartials ||
-      L.num_rows <= 0 || L.num_rows > 0x7FFFFFFF) {
+  const FusedPlan plan = plan_fused(nvec, L.num_partials, L.num_rows, L.num_cus);
+  const int g = plan.geometry;
+  if (g < 0 || L.num_partials < 1 || L.num_partials > kMaxPartials || L.num_rows <= 0 ||
+      L.num_rows > 0x7FFFFFFF || L.num_cus < 1) {
     std::snprintf(err, errlen, "internal: launch shape outside the compiled kernels");
     return (int)hipErrorInvalidValue;
   }
@@ -483,30 +509,26 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
   k.hidden = (float)L.hidden;
   k.eps = L.eps;
 
-  const Geometry geo = fused_geometry(g, L.num_partials);
-  const int block = geo.block;
+  const int block = plan.geo.block;
   hipError_t e;
   if (L.max_workgroups <= 0 || L.max_workgroups >= L.num_rows) {
-    const int64_t round = seq_min_workgroups(block);
+    const int64_t round = plan.round;
     // Dispatches over consecutive row ranges of about equal size, each within
     // the byte and work-item limits; the per-row code is the same in each.
-    const int64_t row_bytes = (int64_t)(L.num_partials + 3) * nvec * 16;
-    const int64_t cap = fused_rows_per_dispatch(block, row_bytes, seq_min_workgroups(block));
-    const int64_t pieces = (L.num_rows + cap - 1) / cap;
-    const int64_t chunk = (L.num_rows + pieces - 1) / pieces;
+    const int64_t chunk = plan.rows_per_dispatch;
     e = hipSuccess;
     for (int64_t r0 = 0; r0 < L.num_rows && e == hipSuccess; r0 += chunk) {
       const int64_t n = L.num_rows - r0 < chunk ? L.num_rows - r0 : chunk;
       k.row_begin = L.row_begin + r0;
       k.row_end = k.row_begin + n;
       // Each dispatch takes its own kernel for its row count (geometry.h).
-      const RowKernel rk = fused_row_kernel(g, L.num_partials, n);
+      const RowKernel rk = fused_row_kernel(g, L.num_partials, n, L.num_cus);
       const KernelFn fn =
-          rk == RowKernel::kStrided
-              ? kStridedTable[bf16][g][L.num_partials - 1]
-              : kTable[bf16][rk == RowKernel::kSequenced][g][L.num_partials - 1];
+          rk == RowKernel::kStrided     ? kStridedTable[bf16][g][L.num_partials - 1]
+          : rk == RowKernel::kBothSlots ? kBothSlotsTable[bf16][g][L.num_partials - 1]
+                                        : kTable[bf16][rk == RowKernel::kSequenced][g][L.num_partials - 1];
       if (fn == nullptr) {
-        std::snprintf(err, errlen, "internal: no strided kernel for this row class");
+        std::snprintf(err, errlen, "internal: no kernel of the chosen form for this row class");
         return (int)hipErrorInvalidValue;
       }
       const int64_t grid = rk == RowKernel::kStrided ? round : n;
@@ -520,7 +542,7 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
   } else {
     const int64_t cap = max_rows_per_dispatch(block);
     const int64_t wgs = L.max_workgroups < cap ? L.max_workgroups : cap;
-    const RowsKernelFn fn = kRowsTable[bf16][wgs >= seq_min_workgroups(block)][g][L.num_partials - 1];
+    const RowsKernelFn fn = kRowsTable[bf16][wgs >= round_rows(block, L.num_cus)][g][L.num_partials - 1];
     int64_t rows_per_wg = (L.num_rows + wgs - 1) / wgs;
     int64_t row_end = L.row_begin + L.num_rows;
     const unsigned grid = (unsigned)((L.num_rows + rows_per_wg - 1) / rows_per_wg);

@@ -5,6 +5,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "geometry.h"
+
 namespace tw {
 
 constexpr int kMaxPartials = 16;
@@ -20,12 +22,11 @@ constexpr int64_t kMaxLaunchWorkItems = 0x7FFFFFFF;
 inline int64_t max_rows_per_dispatch(int block) { return kMaxLaunchWorkItems / block; }
 
 // The most bytes one dispatch of the one-row-per-workgroup fused kernel
-// streams.  Measured on MI355X (N = 8 bf16, inputs and outputs rotated past
-// the MALL): one launch streams 79% of peak at 738 MB (T = 4096, h = 8192),
-// 78.7% at 1.1 GB and 77% at 1.5 GB and beyond, and a 1.5 GB launch takes as
-// long at h = 4096 as at h = 8192.  Longer launches are therefore cut into
-// dispatches over consecutive row ranges of about equal size, none above this
-// many bytes and each at least one round of resident workgroups.
+// streams: single launches lose speed beyond about 768 MiB, in proportion to
+// the bytes rather than the rows (profiles/launch_rules_mi355x.md, "Dispatch
+// size").  Longer launches are therefore cut into dispatches over consecutive
+// row ranges of about equal size, none above this many bytes and each at
+// least one round of resident workgroups.
 constexpr int64_t kMaxDispatchBytes = int64_t(768) << 20;
 
 // Rows per dispatch for rows of row_bytes (all tensors of a row, read and
@@ -38,6 +39,35 @@ inline int64_t fused_rows_per_dispatch(int block, int64_t row_bytes, int64_t rou
   if (cap < round_rows) cap = round_rows;
   const int64_t hard = max_rows_per_dispatch(block);
   return cap < hard ? cap : hard;
+}
+
+// How a fused call of `rows` rows is laid out: its row class and geometry,
+// the round of resident workgroups on num_cus CUs, and the consecutive row
+// ranges of about equal size it is cut into.  geometry < 0: no compiled
+// kernel covers rows of nvec vectors.
+struct FusedPlan {
+  int geometry;
+  Geometry geo;
+  int64_t round;
+  int64_t rows_per_dispatch;
+  int64_t dispatches;
+};
+
+inline FusedPlan plan_fused(int64_t nvec, int num_partials, int64_t rows, int num_cus) {
+  FusedPlan p{};
+  p.geometry = geometry_index(nvec);
+  if (p.geometry < 0 || nvec > kMaxVectors || rows <= 0 || num_cus < 1) {
+    p.geometry = p.geometry < 0 || nvec > kMaxVectors ? -1 : p.geometry;
+    return p;
+  }
+  p.geo = fused_geometry(p.geometry, num_partials);
+  p.round = round_rows(p.geo.block, num_cus);
+  const int64_t row_bytes = (int64_t)(num_partials + 3) * nvec * 16;
+  const int64_t cap = fused_rows_per_dispatch(p.geo.block, row_bytes, p.round);
+  const int64_t pieces = (rows + cap - 1) / cap;
+  p.rows_per_dispatch = (rows + pieces - 1) / pieces;
+  p.dispatches = (rows + p.rows_per_dispatch - 1) / p.rows_per_dispatch;
+  return p;
 }
 
 struct FusedLaunch {
@@ -54,6 +84,7 @@ struct FusedLaunch {
   int32_t dtype;       // tw_dtype value
   void* stream;        // hipStream_t
   int64_t max_workgroups;   // <= 0: one workgroup per row; else at most this many
+  int32_t num_cus;     // CUs the stream's launches may use (sizes a round of workgroups)
 };
 
 // Enqueues the kernel.  Returns 0 on success; otherwise writes a message to
@@ -69,6 +100,7 @@ struct ReduceLaunch {
   int64_t hidden;
   int32_t dtype;
   void* stream;
+  int32_t num_cus;     // CUs the stream's launches may use
 };
 int launch_reduce(const ReduceLaunch& a, char* err, size_t errlen);
 

@@ -259,7 +259,7 @@ int launch_reduce(const ReduceLaunch& L, char* err, size_t errlen) {
   const int64_t nvec = L.hidden * (bf16 ? 2 : 4) / 16;
   const int g = geometry_index(nvec);
   if (const int e = shape_error(nvec, L.num_rows, g, err, errlen)) return e;
-  if (L.num_partials < 1 || L.num_partials > kMaxPartials) {
+  if (L.num_partials < 1 || L.num_partials > kMaxPartials || L.num_cus < 1) {
     std::snprintf(err, errlen, "internal: partial count outside the compiled kernels");
     return (int)hipErrorInvalidValue;
   }
@@ -270,7 +270,7 @@ int launch_reduce(const ReduceLaunch& L, char* err, size_t errlen) {
   const Geometry geo = fused_geometry(g, L.num_partials);
   // The fused kernel's rule for the load order, for a chain of N tensors
   // (the reduce reads no residual).
-  const bool seq = use_sequenced_order(L.num_rows, seq_min_workgroups(geo.block),
+  const bool seq = use_sequenced_order(L.num_rows, round_rows(geo.block, L.num_cus),
                                        L.num_partials - 1, geo.seq);
   const ReduceFn fn = kReduce[bf16][seq][g][L.num_partials - 1];
   // Row ranges of at most max_rows_per_dispatch rows, each its own dispatch

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.mark.parametrize("mode,extra,rows", [
     ("full", [], 1024), ("shard", [], 128),
-    ("full", ["--tokens", "300", "--partials", "3", "--no-split"], 300)])
+    ("full", ["--tokens", "300", "--partials", "3", "--no-split"], 300),
+    ("full", ["--workload", "tiny"], 64)])
 def test_bench_line_keeps_the_contract(mode, extra, rows):
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
@@ -33,16 +34,19 @@ def test_bench_line_keeps_the_contract(mode, extra, rows):
     d = json.loads(lines[0])
     for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
                 "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
-                "roofline", "cpu_baseline"):
+                "roofline", "cpu_baseline", "settle"):
         assert key in d, key
+    assert d["settle"]["steps"] >= 50 and d["settle"]["seconds"] > 0
     assert d["unit"] == "GB/s" and d["n_gpus"] == 1 and d["steps"] == 40 and d["warmup"] == 10
     assert d["higher_is_better"] is True and d["vs_baseline"] is None
     cfg = d["config"]
     assert cfg["rows"] == rows
-    if extra:
+    if "--tokens" in extra:
         assert cfg["num_tokens"] == 300 and cfg["num_partials"] == 3
         assert d["roofline"]["traffic"] is None    # counters belong to the default shape only
-    step_bytes = (cfg["num_partials"] + 3) * rows * cfg["hidden"] * 2
+    itemsize = 2 if cfg["storage_dtype"] == "bf16" else 4
+    assert f"{cfg['storage_dtype']} storage" in cfg["workload"]
+    step_bytes = (cfg["num_partials"] + 3) * rows * cfg["hidden"] * itemsize
     assert abs(d["value"] - step_bytes / (d["ms_per_step"] * 1e-3) / 1e9) <= 0.01 * d["value"]
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"

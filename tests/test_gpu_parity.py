@@ -457,23 +457,45 @@ def test_nan_input_propagates_to_its_row_only():
     check(rout[keep], x, "bf16", "residual_out")
 
 
-@pytest.mark.parametrize("num_cus", [8, 64, 256])
-def test_cu_masked_stream_gives_identical_results(num_cus):
+@pytest.mark.parametrize("num_cus,T,kernel", [(8, 200, "seq"), (64, 150, "all"),
+                                              (64, 200, "seq"), (64, 296, "strided"),
+                                              (256, 200, "all")])
+def test_cu_masked_stream_matches_oracle_and_takes_its_own_round(num_cus, T, kernel):
     # The first k mask bits spread k CUs evenly over the XCDs (bit b belongs to
-    # XCD b mod 8).  Where the workgroups run must not change a single bit.
+    # XCD b mod 8).  The launch rules size a round from the CUs the stream may
+    # use: on 64 CUs a round of 1024-thread workgroups is 128 rows, so 150 rows
+    # (just past one round, N = 8) issue all loads at once, 200 rows load in
+    # sequence and 296 rows (a last round of 40) run the strided kernel, where
+    # the whole device would issue all loads at once for each.  Where the
+    # workgroups run must not change a single bit, and every row must meet
+    # the oracle.
     from reduce_rmsnorm_amd.overlap import MaskedStream, mask_words
-    d = make_inputs("llama70b", num_tokens=200, hidden=8192, seed=7)
+    d = make_inputs("llama70b", num_tokens=T, hidden=8192, seed=7)
     parts, res, w = upload(d)
     ref_out, ref_rout = _run_full(parts, res, w, d["eps"])
-    say(f"fused launch on a stream masked to {num_cus} CUs")
+    say(f"fused launch of {T} rows on a stream masked to {num_cus} CUs")
     with MaskedStream(range(num_cus)) as ms:
         assert ms.mask() == mask_words(range(num_cus))
+        info = tw.tw_fused_launch_info(8, T, 8192, stream=ms.stream)
+        assert (info["num_cus"], info["round_rows"], info["kernel_name"]) == \
+            (num_cus, 2 * num_cus, kernel), info
         out = torch.full_like(res, float("nan"))
         rout = torch.full_like(res, float("nan"))
         tw.PreparedFused(parts, res, w, d["eps"], out, rout, ms.stream)()
         ms.stream.synchronize()
     np.testing.assert_array_equal(to_host(out), ref_out)
     np.testing.assert_array_equal(to_host(rout), ref_rout)
+    y, x, _ = _oracle(d)
+    check(ref_out, y, "bf16", "out")
+    check(ref_rout, x, "bf16", "residual_out")
+
+
+def test_device_cu_count_sizes_the_round():
+    # The null stream and a plain stream may use every CU of the device.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for st in (None, torch.cuda.Stream()):
+        info = tw.tw_fused_launch_info(8, 1024, 8192, stream=st)
+        assert info["num_cus"] == cus and info["round_rows"] == 2 * cus, info
 
 
 def test_row_count_beyond_one_dispatch():
@@ -640,7 +662,8 @@ def test_row_whose_sum_of_squares_overflows_float32():
                                          (2560, 8, "bf16", 3200), (2552, 12, "bf16", 3200),
                                          (3072, 2, "bf16", 1400), (1280, 4, "f32", 3100),
                                          (12288, 8, "bf16", 2200), (12280, 16, "bf16", 2200),
-                                         (2560, 1, "bf16", 1100), (1536, 1, "f32", 1100)])
+                                         (2560, 1, "bf16", 1100), (1536, 1, "f32", 1100),
+                                         (16384, 8, "bf16", 2048)])
 def test_load_order_never_changes_a_bit(h, N, dtype, T):
     # A launch that fills every CU loads the tensors in summation order; a
     # smaller one (here each of the N shards) issues all loads at once.  The
@@ -678,6 +701,37 @@ def test_load_order_never_changes_a_bit(h, N, dtype, T):
     check(rout[rows], x, dtype, "residual_out")
 
 
+@pytest.mark.parametrize("h,N,T", [(16384, 8, 256), (16384, 4, 240), (16384, 11, 250),
+                                   (12288, 4, 256), (16376, 8, 256)])
+def test_both_slots_launch_matches_one_slot_launches_and_oracle(h, N, T):
+    # A launch that gives nearly every CU one workgroup of 1024 x 2 loads
+    # both vector slots at once; the same rows as two launches of half the
+    # rows each load one slot at a time.  Same bits, and every sampled row
+    # meets the oracle (16376 leaves lanes that clamp their address).
+    info = tw.tw_fused_launch_info(N, T, h)
+    cus = info["num_cus"]
+    if not (8 * T > 7 * cus and T <= cus):
+        pytest.skip(f"{T} rows do not give each of {cus} CUs one workgroup")
+    assert info["kernel_name"] == "both" and tw.tw_fused_launch_info(N, T // 2, h)["kernel_name"] == "all"
+    d = make_inputs("llama405b", num_tokens=T, hidden=h, seed=90 + N)
+    d["partials"] = np.concatenate([d["partials"]] + [d["partials"][:, ::-1]] * 2)[:N]
+    parts, res, w = upload(d)
+    say(f"both slots at once: T={T} h={h} N={N}")
+    out, rout = _run_full(parts, res, w, d["eps"])
+    out_p = torch.full_like(res, float("nan"))
+    rout_p = torch.full_like(res, float("nan"))
+    for lo, hi in ((0, T // 2), (T // 2, T)):
+        tw.tw_fused_reduce_rmsnorm(parts[:, lo:hi], res[lo:hi], w, d["eps"], out=out_p[lo:hi],
+                                   residual_out=rout_p[lo:hi])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(out_p), out)
+    np.testing.assert_array_equal(to_host(rout_p), rout)
+    rows = sorted(set(range(0, T, 17)) | {T - 1})
+    y, x, _ = _oracle(d, rows=rows)
+    check(out[rows], y, "bf16", "out")
+    check(rout[rows], x, "bf16", "residual_out")
+
+
 # Launches whose row count is not a whole number of rounds (a round: 512
 # workgroups for the 1024-thread classes, h = 8192 or 16384 bf16 and 4096 or
 # 8192 f32; 1024 for 512 x 1, h = 4096 bf16).  The first nine cases have a
@@ -697,22 +751,13 @@ RAGGED_ROUNDS = [(8192, 8, "bf16", 768), (8192, 5, "bf16", 600), (8192, 16, "bf1
 
 
 def _round_rows(h, elem_bytes, n):
-    """Rows one round of resident workgroups holds, for the sequenced row
-    classes these tests use."""
-    nvec = h * elem_bytes // 16
-    if nvec <= 320:
-        block = 320
-    elif nvec <= 384:
-        block = 384
-    elif nvec <= 512:
-        block = 512
-    elif nvec <= 640:
-        block = 640 if n >= 7 else 1024 if n >= 5 else 512
-    elif 1024 < nvec <= 1536 and n >= 6:
-        block = 512
-    else:
-        block = 1024
-    return 256 * (2048 // block)
+    """Rows one round of resident workgroups holds on this device, for the
+    sequenced row classes these tests use: 2048 threads per CU divided among
+    the row class's workgroups (the fitted 320-, 384- and 640-thread classes
+    and 512 x 3 included), as the library counts it."""
+    info = tw.tw_fused_launch_info(n, 1, h, torch.bfloat16 if elem_bytes == 2 else torch.float32)
+    assert info["round_rows"] == info["num_cus"] * (2048 // info["threads_per_workgroup"])
+    return info["round_rows"]
 
 
 @pytest.mark.parametrize("h,N,dtype,T", RAGGED_ROUNDS)

@@ -4,9 +4,10 @@ sequence, or the strided kernel), checked at the shapes where the choice was
 measured on MI355X.  tests/c/launch_rules.cpp is built with the host
 compiler against the launcher's geometry header; no GPU.
 
-A round is the number of workgroups resident at once: 512 for the
-1024-thread geometries, 1024 for 512 x 1 and 512 x 3, 768 for 640 x 1, 1280
-for 384 x 1 and 1536 for 320 x 1.  The rules:
+A round is the number of workgroups resident at once on the CUs a launch
+may use; on 256 CUs: 512 for the 1024-thread geometries, 1024 for 512 x 1
+and 512 x 3, 768 for 640 x 1, 1280 for 384 x 1 and 1536 for 320 x 1.  The
+rules:
 * below one round, all loads at once (too few rows to fill the CUs);
 * between one and one and a half rounds, all loads at once when each thread
   waits on a chain of 8 or more tensors (N + 1 tensors, one or two in
@@ -15,7 +16,11 @@ for 384 x 1 and 1536 for 320 x 1.  The rules:
   kernel (one round of workgroups, each taking every round-th row), where the
   geometry loads all of a thread's vector slots in one sequence;
 * otherwise the sequenced one-row kernel.
-Geometries without a sequenced order always load everything at once."""
+Geometries without a sequenced order always load everything at once.  The
+1024 x 2 geometry (h = 16384 bf16, and 9216-12288 below six partials) loads
+both of a thread's vector slots at once, rather than one after the other,
+when a launch gives more than seven eighths of the CUs one workgroup each and
+none two, with up to 11 partials ("both")."""
 
 import os
 import shutil
@@ -49,7 +54,10 @@ CASES = {
     (4096, 2, 2, 1100): "strided", (4096, 2, 2, 1300): "strided", (4096, 2, 1, 4096): "all",
     (4096, 2, 6, 1100): "strided", (4096, 2, 7, 1100): "all", (4096, 2, 3, 1100): "strided",
     # h = 16384 bf16: 1024 x 2, one vector slot at a time, no strided kernel
-    (16384, 2, 8, 256): "all", (16384, 2, 8, 512): "seq", (16384, 2, 8, 576): "all",
+    (16384, 2, 8, 256): "both", (16384, 2, 8, 224): "all", (16384, 2, 8, 225): "both",
+    (16384, 2, 8, 257): "all", (16384, 2, 11, 256): "both", (16384, 2, 12, 256): "all",
+    (16384, 2, 4, 240): "both", (12288, 2, 4, 256): "both", (12288, 2, 8, 256): "all",
+    (16384, 2, 8, 128): "all", (16384, 2, 8, 512): "seq", (16384, 2, 8, 576): "all",
     (16384, 2, 8, 640): "all", (16384, 2, 8, 768): "seq", (16384, 2, 8, 1100): "seq",
     (16384, 2, 1, 2048): "all",
     # float32: h = 4096 is the 1024 x 1 class, h = 8192 the 1024 x 2 class
@@ -82,8 +90,8 @@ def rules_exe(tmp_path_factory):
     return exe
 
 
-def _run(exe, cases):
-    stdin = "".join(f"{h} {es} {n} {rows}\n" for h, es, n, rows in cases)
+def _run(exe, cases, cus=256):
+    stdin = "".join(f"{h} {es} {n} {rows} {cus}\n" for h, es, n, rows in cases)
     out = subprocess.run([exe], input=stdin, check=True, capture_output=True, text=True).stdout
     return [line.split() for line in out.splitlines()]
 
@@ -121,3 +129,68 @@ def test_strided_kernel_only_within_four_rounds_with_a_short_last_round(rules_ex
         everything = rows < 512 or 512 < rows < 768
         want = "strided" if strided else "all" if everything else "seq"
         assert g[0] == want, (rows, g[0], want)
+
+
+@pytest.mark.parametrize("cus", [8, 32, 64, 128, 192, 255, 256, 304])
+def test_rules_scale_with_the_cu_count(rules_exe, cus):
+    # The same rules on any CU count: the round is cus x (2048 / threads), so
+    # a 1024-thread class holds 2 rows per CU, and every row count from 1 to
+    # 5 rounds takes the kernel the rules give for that round.
+    rnd = 2 * cus
+    cases = [(8192, 2, 8, r) for r in range(1, 5 * rnd + 1)]
+    for (h, es, n, rows), g in zip(cases, _run(rules_exe, cases, cus)):
+        assert g[1:] == ["1024", "1", str(rnd)]
+        tail = rows % rnd
+        strided = rnd < rows < 4 * rnd and 0 < tail and 2 * tail <= rnd and 2 * rows >= 3 * rnd
+        everything = rows < rnd or rnd < rows and 2 * rows < 3 * rnd
+        want = "strided" if strided else "all" if everything else "seq"
+        assert g[0] == want, (cus, rows, g[0], want)
+
+
+def test_measured_shapes_scale_with_the_cu_count(rules_exe):
+    # Scaling a 256-CU case's rows by cus / 256 (whole rounds stay whole)
+    # gives the same kernel on cus CUs.
+    keys = [k for k in CASES if k[3] % 4 == 0]
+    for cus in (64, 128):
+        scaled = [(h, es, n, rows * cus // 256) for h, es, n, rows in keys]
+        got = _run(rules_exe, scaled, cus)
+        bad = [(k, CASES[k], g[0]) for k, g in zip(keys, got) if g[0] != CASES[k]]
+        assert not bad, (cus, bad)
+
+
+def test_library_launch_info_matches_the_rules(rules_exe):
+    # The library's own view of a launch (tw_fused_launch_info) takes the
+    # same rules: checked against the rule program at the measured shapes, on
+    # the CU count the library counts for the null stream (every CU of the
+    # device; 256 where the runtime cannot say, as without a GPU).
+    import torch
+    import reduce_rmsnorm_amd as tw
+    first = tw.tw_fused_launch_info(8, 1024, 8192)
+    cus = first["num_cus"]
+    keys = list(CASES)
+    got = _run(rules_exe, keys, cus)
+    for (h, es, n, rows), g in zip(keys, got):
+        info = tw.tw_fused_launch_info(n, rows, h, torch.bfloat16 if es == 2 else torch.float32)
+        assert info["num_cus"] == cus
+        assert (info["threads_per_workgroup"], info["vectors_per_thread"], info["round_rows"]) == \
+            (int(g[1]), int(g[2]), int(g[3]))
+        if info["dispatches"] == 1:
+            assert info["kernel_name"] == g[0], (h, es, n, rows)
+    if cus == 256:
+        assert [(k, tw.tw_fused_launch_info(k[2], k[3], k[0])["kernel_name"]) for k in
+                [(8192, 2, 8, 1024), (8192, 2, 8, 700), (8192, 2, 8, 1280)]] == \
+            [((8192, 2, 8, 1024), "seq"), ((8192, 2, 8, 700), "all"), ((8192, 2, 8, 1280), "strided")]
+
+
+def test_library_launch_info_cuts_long_calls():
+    import reduce_rmsnorm_amd as tw
+    info = tw.tw_fused_launch_info(8, 70_000_000, 8)          # 16-byte rows, N = 8
+    assert info["dispatches"] > 1
+    assert info["rows_per_dispatch"] * info["dispatches"] >= 70_000_000
+    assert info["rows_per_dispatch"] * info["threads_per_workgroup"] <= 2 ** 31 - 1
+    none = tw.tw_fused_launch_info(8, 0, 8192)
+    assert (none["dispatches"], none["rows_per_dispatch"], none["kernel"]) == (0, 0, -1)
+    with pytest.raises(tw.TokenWeaveError):
+        tw.tw_fused_launch_info(0, 10, 8192)
+    with pytest.raises(tw.TokenWeaveError):
+        tw.tw_fused_launch_info(8, 10, 12)
