@@ -120,6 +120,10 @@ def parse():
                     help="also run the fused kernel on CU-masked streams: where mask bits land "
                          "(XCD, CU), GB/s against the number of CUs, and the split layer step "
                          "with the fused kernel and the GEMM on disjoint CU sets")
+    ap.add_argument("--host-cost", action="store_true",
+                    help="also time the host side of one call through the binding (eager with "
+                         "stacked or listed partials, prepared, shard, split plan lookup) on a "
+                         "64-row launch the GPU keeps up with")
     ap.add_argument("--launch-floor", action="store_true",
                     help="also time an empty kernel of 1, 256, 1024 and 4096 workgroups, "
                          "replayed from a HIP graph: the fixed cost of a dependent launch")
@@ -212,6 +216,45 @@ def run_ceiling(tw, sets, R, rows, h, itemsize, stream, steps, timer):
             print(f"[bench] schedule twin {key} ({res['twin_load_order']}): {nbytes} B in "
                   f"{us:.2f} us = {res[key + '_gbs']} GB/s", file=sys.stderr, flush=True)
     return res
+
+
+HOST_COST_CALLS = 3000
+
+
+def run_host_cost(tw, torch, wl, sets, w, stream, plan_kw) -> dict:
+    """Host time per call of the binding, on 64-row launches (a few µs of GPU
+    work each, so the GPU keeps up and the host never waits on a full queue):
+    the mean wall time of HOST_COST_CALLS back-to-back calls, no
+    synchronization inside the loop."""
+    parts, res, out, rout = sets[0]
+    p64, r64, o64, ro64 = parts[:, :64], res[:64], out[:64], rout[:64]
+    listed = [parts[i, :64] for i in range(parts.shape[0])]
+    prepared = tw.PreparedFused(p64, r64, w, wl.eps, o64, ro64, stream)
+    cache = tw.SplitPlanCache(**plan_kw)
+    calls = {
+        "eager_stacked": lambda: tw.tw_fused_reduce_rmsnorm(p64, r64, w, wl.eps, out=o64,
+                                                            residual_out=ro64),
+        "eager_listed": lambda: tw.tw_fused_reduce_rmsnorm(listed, r64, w, wl.eps, out=o64,
+                                                           residual_out=ro64),
+        "eager_shard": lambda: tw.tw_shard_rmsnorm(p64, r64, w, wl.eps, 0, out=o64,
+                                                   residual_out=ro64),
+        "prepared": prepared,
+        "split_plan_cached": lambda: cache(wl.num_tokens),
+        "split_plan_c": lambda: tw.tw_split_plan(wl.num_tokens, **plan_kw),
+    }
+    res_us = {}
+    for name, fn in calls.items():
+        for _ in range(200):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(HOST_COST_CALLS):
+            fn()
+        us = (time.perf_counter() - t0) * 1e6 / HOST_COST_CALLS
+        torch.cuda.synchronize()
+        res_us[name] = round(us, 2)
+        print(f"[bench] host cost {name}: {us:.2f} us per call", file=sys.stderr, flush=True)
+    return {"calls": HOST_COST_CALLS, "rows": 64, "us_per_call": res_us}
 
 
 def run_launch_floor(torch, timer) -> dict:
@@ -893,6 +936,9 @@ def main():
     if args.ceiling:
         ceiling = run_ceiling(tw, sets, R, rows, h, wl.itemsize, stream, min(args.steps, 500),
                               timer)
+    host_cost = None
+    if args.host_cost:
+        host_cost = run_host_cost(tw, torch, wl, sets, w, stream, plan_kw)
     launch_floor = None
     if args.launch_floor:
         launch_floor = run_launch_floor(torch, timer)
@@ -948,6 +994,8 @@ def main():
         result["ramp"] = ramp
     if launch_floor is not None:
         result["empty_launch_us"] = launch_floor
+    if host_cost is not None:
+        result["host_cost"] = host_cost
     if staircase is not None:
         result["gemm_staircase"] = staircase
     if ceiling is not None:

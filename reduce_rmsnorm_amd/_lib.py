@@ -149,36 +149,85 @@ def _as_list(partials: Union[torch.Tensor, Sequence[torch.Tensor]]):
 
 
 def _marshal(partials, residual, weight, out, residual_out):
-    parts = _as_list(partials)
-    if not parts:
-        raise ValueError("at least one partial is required")
+    """Checks the tensors and returns (N, pointer array, T, h, out,
+    residual_out).  Every tensor must be a contiguous [T, h] (weight: [h])
+    tensor of the residual's dtype on the residual's GPU; ``partials`` is a
+    list of [T, h] tensors or one [N, T, h] tensor whose [T, h] slices are
+    contiguous (a stacked tensor is checked once, not per partial)."""
     if residual.dim() != 2:
         raise ValueError("residual must be [T, h]")
-    T, h = residual.shape
-    for t in parts + [residual, weight]:
-        if not t.is_cuda:
-            raise ValueError("every tensor must be on a GPU (there is no CPU path)")
-        if t.device != residual.device:
-            raise ValueError("every tensor must be on the residual's GPU")
-        if t.dtype != residual.dtype:
+    shape, dt, dev = residual.shape, residual.dtype, residual.device
+    T, h = shape
+    if isinstance(partials, torch.Tensor):
+        if partials.dim() != 3:
+            raise ValueError("a stacked partials tensor must be [N, T, h]")
+        n = partials.shape[0]
+        if n < 1:
+            raise ValueError("at least one partial is required")
+        if partials.shape[1:] != shape:
+            raise ValueError(f"partial shape {tuple(partials.shape[1:])} != residual shape {(T, h)}")
+        if partials.device != dev or dev.type != "cuda":
+            raise ValueError("every tensor must be on the residual's GPU (there is no CPU path)")
+        if partials.dtype is not dt:
             raise ValueError("every tensor must share one dtype")
-        if not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
-    for p in parts:
-        if tuple(p.shape) != (T, h):
-            raise ValueError(f"partial shape {tuple(p.shape)} != residual shape {(T, h)}")
-    if tuple(weight.shape) != (h,):
+        if T * h > 0 and (partials.stride(2) != 1 or (T > 1 and partials.stride(1) != h)):
+            raise ValueError("tensors must be contiguous (each [T, h] slice of the partials)")
+        step = partials.stride(0) * partials.element_size()
+        base = partials.data_ptr()
+        ptrs = (ctypes.c_void_p * n)(*range(base, base + n * step, step)) if step else \
+            (ctypes.c_void_p * n)(*([base] * n))
+    else:
+        parts = list(partials)
+        n = len(parts)
+        if not parts:
+            raise ValueError("at least one partial is required")
+        for q in parts:
+            if q.shape != shape:
+                raise ValueError(f"partial shape {tuple(q.shape)} != residual shape {(T, h)}")
+            if q.device != dev or dev.type != "cuda":
+                raise ValueError("every tensor must be on the residual's GPU (there is no CPU path)")
+            if q.dtype is not dt:
+                raise ValueError("every tensor must share one dtype")
+            if not q.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+        ptrs = (ctypes.c_void_p * n)(*[q.data_ptr() for q in parts])
+    if dev.type != "cuda" or weight.device != dev:
+        raise ValueError("every tensor must be on a GPU, the residual's (there is no CPU path)")
+    if weight.dtype is not dt:
+        raise ValueError("every tensor must share one dtype")
+    if weight.shape != (h,):
         raise ValueError("weight must be [h]")
+    if not residual.is_contiguous() or not weight.is_contiguous():
+        raise ValueError("tensors must be contiguous")
     if out is None:
         out = torch.empty_like(residual)
     if residual_out is None:
         residual_out = torch.empty_like(residual)
     for t in (out, residual_out):
-        if tuple(t.shape) != (T, h) or t.dtype != residual.dtype or not t.is_contiguous() \
-                or t.device != residual.device:
+        if t.shape != shape or t.dtype is not dt or t.device != dev or not t.is_contiguous():
             raise ValueError("out and residual_out must be contiguous [T, h] tensors like residual")
-    ptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
-    return parts, ptrs, T, h, out, residual_out
+    return n, ptrs, T, h, out, residual_out
+
+
+class _on_device:
+    """Makes the tensors' GPU the current device for the call, and does
+    nothing when it already is (the common case, which then costs no
+    device switch)."""
+
+    __slots__ = ("_ctx",)
+
+    def __init__(self, device: torch.device):
+        self._ctx = None
+        if device.index is not None and device.index != torch.cuda.current_device():
+            self._ctx = torch.cuda.device(device)
+
+    def __enter__(self):
+        if self._ctx is not None:
+            self._ctx.__enter__()
+
+    def __exit__(self, *exc):
+        if self._ctx is not None:
+            self._ctx.__exit__(*exc)
 
 
 def _stream_handle(device: torch.device, stream: Optional[torch.cuda.Stream]):
@@ -196,9 +245,9 @@ def tw_fused_reduce_rmsnorm(partials, residual: torch.Tensor, weight: torch.Tens
     ``(out, residual_out)``.  ``partials`` is a list of [T, h] tensors or one
     stacked [N, T, h] tensor."""
     lib = load_library()
-    parts, ptrs, T, h, out, residual_out = _marshal(partials, residual, weight, out, residual_out)
-    with torch.cuda.device(residual.device):
-        _check(lib.tw_fused_reduce_rmsnorm(ptrs, len(parts), residual.data_ptr(), weight.data_ptr(),
+    n, ptrs, T, h, out, residual_out = _marshal(partials, residual, weight, out, residual_out)
+    with _on_device(residual.device):
+        _check(lib.tw_fused_reduce_rmsnorm(ptrs, n, residual.data_ptr(), weight.data_ptr(),
                                            out.data_ptr(), residual_out.data_ptr(), T, h,
                                            float(eps), _dtype_code(residual),
                                            _stream_handle(residual.device, stream)))
@@ -213,9 +262,9 @@ def tw_fused_reduce_rmsnorm_grid(partials, residual: torch.Tensor, weight: torch
     """The fused step on at most ``num_workgroups`` workgroups, each taking
     ceil(T / G) consecutive rows; bit-identical to tw_fused_reduce_rmsnorm."""
     lib = load_library()
-    parts, ptrs, T, h, out, residual_out = _marshal(partials, residual, weight, out, residual_out)
-    with torch.cuda.device(residual.device):
-        _check(lib.tw_fused_reduce_rmsnorm_grid(ptrs, len(parts), residual.data_ptr(),
+    n, ptrs, T, h, out, residual_out = _marshal(partials, residual, weight, out, residual_out)
+    with _on_device(residual.device):
+        _check(lib.tw_fused_reduce_rmsnorm_grid(ptrs, n, residual.data_ptr(),
                                                 weight.data_ptr(), out.data_ptr(),
                                                 residual_out.data_ptr(), T, h, float(eps),
                                                 _dtype_code(residual), int(num_workgroups),
@@ -231,9 +280,9 @@ def tw_shard_rmsnorm(partials, residual: torch.Tensor, weight: torch.Tensor, eps
     buffers (N = number of partials); other rows of out/residual_out are left
     as they were."""
     lib = load_library()
-    parts, ptrs, T, h, out, residual_out = _marshal(partials, residual, weight, out, residual_out)
-    with torch.cuda.device(residual.device):
-        _check(lib.tw_shard_rmsnorm(ptrs, len(parts), residual.data_ptr(), weight.data_ptr(),
+    n, ptrs, T, h, out, residual_out = _marshal(partials, residual, weight, out, residual_out)
+    with _on_device(residual.device):
+        _check(lib.tw_shard_rmsnorm(ptrs, n, residual.data_ptr(), weight.data_ptr(),
                                     out.data_ptr(), residual_out.data_ptr(), T, h, float(eps),
                                     _dtype_code(residual), int(shard_index),
                                     _stream_handle(residual.device, stream)))
@@ -282,7 +331,7 @@ def tw_reduce_partials(partials, reduced: Optional[torch.Tensor] = None,
         raise ValueError("reduced must be a contiguous tensor like the partials")
     T, h = ref.shape
     ptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
-    with torch.cuda.device(ref.device):
+    with _on_device(ref.device):
         _check(lib.tw_reduce_partials(ptrs, len(parts), reduced.data_ptr(), T, h,
                                       _dtype_code(ref), _stream_handle(ref.device, stream)))
     return reduced
@@ -294,7 +343,7 @@ def tw_add_rmsnorm(inp: torch.Tensor, residual: torch.Tensor, weight: torch.Tens
     """Unfused comparator, step 2: standard two-pass residual-add + RMSNorm."""
     lib = load_library()
     _, _, T, h, out, residual_out = _marshal([inp], residual, weight, out, residual_out)
-    with torch.cuda.device(residual.device):
+    with _on_device(residual.device):
         _check(lib.tw_add_rmsnorm(inp.data_ptr(), residual.data_ptr(), weight.data_ptr(),
                                   out.data_ptr(), residual_out.data_ptr(), T, h, float(eps),
                                   _dtype_code(residual), _stream_handle(residual.device, stream)))
@@ -374,7 +423,6 @@ def tw_fused_reduce_rmsnorm_split(partials, residual: torch.Tensor, weight: torc
                                   stream: Optional[torch.cuda.Stream] = None):
     """Split execution: two launches, rows [0, P) then [P, T), on one stream.
     The suffix launch gets every pointer advanced by P rows."""
-    parts = _as_list(partials)
     T = residual.shape[0]
     if not 0 <= prefix_tokens <= T:
         raise ValueError("prefix_tokens must lie in [0, T]")
@@ -383,8 +431,11 @@ def tw_fused_reduce_rmsnorm_split(partials, residual: torch.Tensor, weight: torc
     if residual_out is None:
         residual_out = torch.empty_like(residual)
     P = int(prefix_tokens)
+    stacked = isinstance(partials, torch.Tensor) and partials.dim() == 3
+    parts = partials if stacked else _as_list(partials)
     for lo, hi in ((0, P), (P, T)):
-        tw_fused_reduce_rmsnorm([p[lo:hi] for p in parts], residual[lo:hi], weight, eps,
+        piece = parts[:, lo:hi] if stacked else [p[lo:hi] for p in parts]
+        tw_fused_reduce_rmsnorm(piece, residual[lo:hi], weight, eps,
                                 out=out[lo:hi], residual_out=residual_out[lo:hi], stream=stream)
     return out, residual_out
 
@@ -403,11 +454,11 @@ class PreparedFused:
                  residual_out: torch.Tensor, stream: Optional[torch.cuda.Stream] = None,
                  mode: str = "full", shard_index: int = 0, num_workgroups: int = 0):
         lib = load_library()
-        parts, ptrs, T, h, out, residual_out = _marshal(partials, residual, weight, out,
-                                                        residual_out)
-        self._keep = (parts, residual, weight, out, residual_out, ptrs, stream)
+        n, ptrs, T, h, out, residual_out = _marshal(partials, residual, weight, out,
+                                                    residual_out)
+        self._keep = (partials, residual, weight, out, residual_out, ptrs, stream)
         self.out, self.residual_out = out, residual_out
-        head = (ptrs, len(parts), residual.data_ptr(), weight.data_ptr(), out.data_ptr(),
+        head = (ptrs, n, residual.data_ptr(), weight.data_ptr(), out.data_ptr(),
                 residual_out.data_ptr(), T, h, ctypes.c_float(float(eps)), _dtype_code(residual))
         s = _stream_handle(residual.device, stream)
         if mode == "full":

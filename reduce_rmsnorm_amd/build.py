@@ -41,6 +41,14 @@ HIP_SOURCES = ["fused_reduce_rmsnorm.hip", "unfused.hip"]
 # argument block.
 HIP_SOURCE_FLAGS = {"fused_reduce_rmsnorm.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=3"],
                     "unfused.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"]}
+# The compiler's per-kernel resource report (registers, scratch, occupancy) of
+# each kernel source, kept next to its object for the spill checks of the
+# tests.
+RESOURCE_FLAGS = ["-Rpass-analysis=kernel-resource-usage"]
+
+
+def resource_report(src: str) -> str:
+    return os.path.join(BUILD, src + ".resources.txt")
 # Measurement-only bandwidth probes (bench.py --ceiling, counter calibration),
 # built into a library of their own so the fused library carries none of them.
 PROBE_SOURCE = "bw_probe.hip"
@@ -54,15 +62,23 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP extension cannot be built")
 
 
-def _run_all(cmds):
+def _run_all(cmds, logs=None):
+    """Runs the commands in parallel.  A command whose index has a path in
+    ``logs`` writes its output there (the resource-usage remarks) instead of
+    to stderr."""
+    logs = logs or {}
     procs = [(c, subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
              for c in cmds]
     failed = []
-    for c, p in procs:
+    for i, (c, p) in enumerate(procs):
         out, _ = p.communicate()
         # hipcc's host pass does not know the packed-fp32 target feature; harmless.
         lines = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln
                  and "is not a recognized feature for this target" not in ln]
+        if i in logs:
+            with open(logs[i], "w") as f:
+                f.write("\n".join(lines) + "\n")
+            lines = [ln for ln in lines if "error" in ln] if p.returncode != 0 else []
         if lines:
             sys.stderr.write("\n".join(lines) + "\n")
         if p.returncode != 0:
@@ -80,11 +96,12 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD, src + ".o")
         cmds.append(["g++", *CXX_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    logs = {}
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        cmds.append([hipcc, *HIP_FLAGS, *HIP_SOURCE_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC,
-                     "-c", os.path.join(CSRC, src),
-                     "-o", obj])
+        logs[len(cmds)] = resource_report(src)
+        cmds.append([hipcc, *HIP_FLAGS, *HIP_SOURCE_FLAGS.get(src, []), *RESOURCE_FLAGS, "-I",
+                     INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     if verbose:
         for c in cmds:
@@ -94,7 +111,7 @@ def build(verbose: bool = False) -> str:
                  probe_obj])
     if verbose:
         print(" ".join(cmds[-1]))
-    _run_all(cmds)
+    _run_all(cmds, logs)
     tmp, ptmp = LIB_PATH + ".tmp", PROBE_LIB_PATH + ".tmp"
     _run_all([[hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs],
               [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", ptmp, probe_obj]])

@@ -86,6 +86,8 @@ def stats(path: str, command: str, out: str) -> None:
     med = _medians(trace) if trace != path and os.path.exists(trace) else {}
     lines = [f"# rocprofv3 kernel statistics: {os.path.basename(out)[:-3]}", "",
              "Command (run from /tmp with TMPDIR=/tmp, repo at $R):", "", "```", command, "```", "",
+             "Kernel code sha256 (kernel source and headers with comments and whitespace removed, "
+             f"and the compile flags): `{kernel_code_hash()}`", "",
              "| Kernel | Calls | Avg us | Median us | Min us | Max us | StdDev us | % time |",
              "|---|---|---|---|---|---|---|---|"]
     for r in rows:
