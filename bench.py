@@ -71,6 +71,10 @@ def parse():
                          "same steps (which always runs, so that the GPU has reached its "
                          "steady speed under load before the timed steps)"
                          % (1e3 * SETTLE_SECONDS))
+    ap.add_argument("--settle-ms", type=float, default=1e3 * SETTLE_SECONDS,
+                    help="GPU work, in ms, of the settle that precedes the warm-up (default "
+                         "%(default)s; counter passes under a profiler, which serializes every "
+                         "dispatch, set 0)")
     ap.add_argument("--ramp", action="store_true",
                     help="also time the first %d steps after a short pause, in blocks of %d: "
                          "the ramp that the warm-up covers" % (RAMP_BLOCKS * RAMP_BLOCK,
@@ -775,7 +779,7 @@ def main():
     # The settle: steps enough for about SETTLE_SECONDS of GPU work (estimated
     # at the bytes at 6 TB/s plus 3 us per launch), then the requested warm-up.
     est = step_bytes / 6.0e12 + 3e-6 * len(launches_per_set[0])
-    settle_steps = max(50, math.ceil(SETTLE_SECONDS / est))
+    settle_steps = max(50, math.ceil(args.settle_ms * 1e-3 / est)) if args.settle_ms > 0 else 0
     print(f"[bench] workload={wl.name} mode={args.mode} rows={rows} h={h} N={N} {wl.dtype} "
           f"rotate={R} settle={settle_steps} warmup={args.warmup} steps={args.steps} "
           f"{'graph' if args.graph else 'eager'}", file=sys.stderr, flush=True)
@@ -784,7 +788,8 @@ def main():
     for i in range(settle_steps):
         step(i)
     torch.cuda.synchronize()
-    settle = {"steps": settle_steps, "seconds": round(time.perf_counter() - t_settle, 4)}
+    settle = {"steps": settle_steps, "seconds": round(time.perf_counter() - t_settle, 4),
+              "target_ms": args.settle_ms}
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()

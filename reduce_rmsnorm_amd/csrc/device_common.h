@@ -50,6 +50,19 @@ __device__ __forceinline__ u32x4 pack(const float* f) {
   return v;
 }
 
+// Store of one 16-byte vector, vector index `vec` of a row that starts at
+// `row` and holds `row_bytes` bytes, as a buffer store with the streaming bit
+// (nt) and the device-scope coherence bit (sc1): the line is written through
+// the XCD's L2 instead of staying there dirty until it is evicted, which
+// streams the outputs faster alongside the reads.  Every caller's offset lies
+// inside the row.
+constexpr int kRawBufferFlags = 0x00020000;   // word 3 of a raw buffer resource on gfx9
+constexpr int kStoreSc1Nt = 16 | 2;           // cache-policy bits: sc1, nt
+__device__ __forceinline__ void store_stream(const u32x4& v, u32x4* row, int vec, int row_bytes) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(row, 0, row_bytes, kRawBufferFlags);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, vec * 16, 0, kStoreSc1Nt);
+}
+
 // s + b = t + e exactly (Knuth's TwoSum); the error e is added to c.
 __device__ __forceinline__ void two_sum_into(float& s, float& c, float b) {
   const float t = s + b;

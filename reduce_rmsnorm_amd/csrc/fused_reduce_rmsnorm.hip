@@ -47,8 +47,9 @@
 //    on the launch or its load order), so a row gives the same bits whichever
 //    launch (full, shard, split, grid) runs it.
 //  * Partials and residual are streamed with non-temporal loads, the outputs
-//    with non-temporal stores; the weight row (read by every workgroup) uses
-//    ordinary loads so it stays in L2.
+//    with non-temporal stores that write through the L2 (store_stream); the
+//    weight row (read by every workgroup) uses ordinary loads so it stays in
+//    L2.
 //  * The one-row-per-workgroup kernel takes the first tensor's address, the
 //    first row and the row length as leading scalar arguments, which this
 //    file's build preloads into SGPRs at wave launch (kernel-argument
@@ -103,7 +104,7 @@ _Pragma("unroll")                                                               
       keep[e] = BF16 ? round_to_odd((S)[e], (C)[e], xe) : xe;                          \
     }                                                                                  \
     if (valid[J])                                                                      \
-      __builtin_nontemporal_store(pack<BF16>(keep), a.residual_out + base + vi[J]);    \
+      store_stream(pack<BF16>(keep), a.residual_out + base, vi[J], nvec * 16);         \
 _Pragma("unroll")                                                                      \
     for (int e = 0; e < E; ++e) ss = __builtin_fmaf(x[J][e], x[J][e], ss);             \
   }
@@ -159,7 +160,7 @@ _Pragma("unroll")                                                               
     unpack<BF16>(wraw[j], w);                                                          \
 _Pragma("unroll")                                                                      \
     for (int e = 0; e < E; ++e) y[e] = (x[j][e] * rs) * w[e];                          \
-    if (valid[j]) __builtin_nontemporal_store(pack<BF16>(y), a.out + base + vi[j]);    \
+    if (valid[j]) store_stream(pack<BF16>(y), a.out + base, vi[j], nvec * 16);         \
   }
 
 // The per-row body of both fused kernels: everything the fused step does to

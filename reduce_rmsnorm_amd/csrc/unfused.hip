@@ -139,7 +139,7 @@ void reduce_kernel(const u32x4* k_first, int32_t k_nvec, ReduceArgs a) {
         const float xe = s[jj][e] + c[jj][e];
         keep[e] = BF16 ? round_to_odd(s[jj][e], c[jj][e], xe) : xe;
       }
-      if (valid[j0 + jj]) a.reduced[base + vi[j0 + jj]] = pack<BF16>(keep);
+      if (valid[j0 + jj]) store_stream(pack<BF16>(keep), a.reduced + base, vi[j0 + jj], nvec * 16);
     }
   }
 }
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(BLOCK) void add_rmsnorm_kernel(AddNormArgs a) {
     unpack<BF16>(wr, w);
 #pragma unroll
     for (int e = 0; e < E; ++e) y[e] = (x[e] * rs) * w[e];
-    if (valid[j]) a.out[base + vi[j]] = pack<BF16>(y);
+    if (valid[j]) store_stream(pack<BF16>(y), a.out + base, vi[j], nvec * 16);
   }
 }
 
