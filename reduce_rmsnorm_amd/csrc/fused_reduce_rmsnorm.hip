@@ -91,6 +91,16 @@ struct KArgs {
 // Partial 0 is k_first, the kernel's own (preloaded) copy of its address.
 #define TW_TENSOR(I) ((I) == 0 ? k_first : (I) < N ? a.partials[(I) < N ? (I) : 0] : a.residual)
 
+// Store of an output vector VEC of the row at `base`: written through the L2
+// (store_stream) where the kernel's constant WT says so, else a plain
+// non-temporal store (the strided kernel's many-partial forms, where the
+// buffer store's offset register would spill at the occupancy cap).
+#define TW_STORE(V, TENSOR, VEC)                                                       \
+  {                                                                                    \
+    if constexpr (WT) store_stream((V), (TENSOR) + base, (VEC), nvec * 16);           \
+    else __builtin_nontemporal_store((V), (TENSOR) + base + (VEC));                    \
+  }
+
 // Finishing one vector slot J from its compensated pair (S, C): x, the stored
 // residual (correctly rounded for bf16) and the slot's share of the sum of
 // squares, added in slot order.
@@ -103,8 +113,7 @@ _Pragma("unroll")                                                               
       x[J][e] = valid[J] ? xe : 0.0f;                                                  \
       keep[e] = BF16 ? round_to_odd((S)[e], (C)[e], xe) : xe;                          \
     }                                                                                  \
-    if (valid[J])                                                                      \
-      store_stream(pack<BF16>(keep), a.residual_out + base, vi[J], nvec * 16);         \
+    if (valid[J]) TW_STORE(pack<BF16>(keep), a.residual_out, vi[J])                    \
 _Pragma("unroll")                                                                      \
     for (int e = 0; e < E; ++e) ss = __builtin_fmaf(x[J][e], x[J][e], ss);             \
   }
@@ -160,7 +169,7 @@ _Pragma("unroll")                                                               
     unpack<BF16>(wraw[j], w);                                                          \
 _Pragma("unroll")                                                                      \
     for (int e = 0; e < E; ++e) y[e] = (x[j][e] * rs) * w[e];                          \
-    if (valid[j]) store_stream(pack<BF16>(y), a.out + base, vi[j], nvec * 16);         \
+    if (valid[j]) TW_STORE(pack<BF16>(y), a.out, vi[j])                                \
   }
 
 // The per-row body of both fused kernels: everything the fused step does to
@@ -276,6 +285,7 @@ void fused_reduce_rmsnorm_kernel(const u32x4* k_first, int64_t k_row_begin, int3
                                  KArgs a) {
   constexpr int E = Elem<BF16>::kPerVec;
   constexpr int NW = BLOCK / 64;
+  constexpr bool WT = true;
   __shared__ float wave_part[NW];
   TW_FUSED_ROW_BODY(k_row_begin + blockIdx.x)
 }
@@ -300,6 +310,7 @@ void fused_reduce_rmsnorm_strided_kernel(const u32x4* k_first, int64_t k_row_beg
   static_assert(SEQ > 0 && CHUNK == VPT, "the strided kernel loads all slots in one sequence");
   constexpr int E = Elem<BF16>::kPerVec;
   constexpr int NW = BLOCK / 64;
+  constexpr bool WT = N <= 9;
   __shared__ float wave_part[2][NW];
   const int tid = threadIdx.x;
   const int nvec = k_nvec;
@@ -365,6 +376,7 @@ __global__ __launch_bounds__(BLOCK) void fused_reduce_rmsnorm_rows_kernel(KArgs 
                                                                           int64_t row_end) {
   constexpr int E = Elem<BF16>::kPerVec;
   constexpr int NW = BLOCK / 64;
+  constexpr bool WT = true;
   __shared__ float wave_part[NW];
   const u32x4* const k_first = a.partials[0];
   const int32_t k_nvec = a.nvec;

@@ -59,9 +59,12 @@ constexpr Geometry fused_geometry(int g, int n) {
 // Occupancy of the short form (all loads at once, the form of launches too
 // small for the sequenced order): the geometry's cap up to kMaxCappedPartials,
 // none above, where holding every tensor of a slot at once would spill under
-// the cap.
+// the cap.  1024 x 2 (two slots' sums beside one slot's nine tensors) already
+// needs a few registers more than the cap leaves at kMaxCappedPartials.
 constexpr int short_form_waves_per_eu(int g, int n) {
-  return n <= kMaxCappedPartials ? fused_geometry(g, n).waves_per_eu : 1;
+  const Geometry geo = fused_geometry(g, n);
+  const bool wide = geo.block == 1024 && geo.vpt == 2;
+  return n < kMaxCappedPartials || (n == kMaxCappedPartials && !wide) ? geo.waves_per_eu : 1;
 }
 
 // The sequenced geometries run at 8 waves per SIMD, 4 SIMDs per CU.
