@@ -203,7 +203,7 @@ def run_ceiling(tw, sets, R, rows, h, itemsize, stream, steps, timer):
                                    torch.bfloat16 if itemsize == 2 else torch.float32, stream)
     if row_vecs in (512, 1024, 2048) and info["vectors_per_thread"] * \
             info["threads_per_workgroup"] == row_vecs:
-        seq = 1 if info["kernel_name"] != "all" else 0
+        seq = 1 if info["kernel_name"] in ("seq", "strided") else 0
         res["twin_load_order"] = "sequenced" if seq else "all at once"
         for kind, key, nbytes in ((5, "twin_read_write", (nsrc + 2) * tensor_bytes),
                                   (6, "twin_read_only", nsrc * tensor_bytes)):
@@ -234,6 +234,13 @@ def run_host_cost(tw, torch, wl, sets, w, stream, plan_kw) -> dict:
     p64, r64, o64, ro64 = parts[:, :64], res[:64], out[:64], rout[:64]
     listed = [parts[i, :64] for i in range(parts.shape[0])]
     prepared = tw.PreparedFused(p64, r64, w, wl.eps, o64, ro64, stream)
+    # The C side of a prepared call without the launch: zero rows return right
+    # after the argument checks; the launch description adds the stream's CU
+    # count and the launch plan.
+    prepared_empty = tw.PreparedFused(parts[:, :0], res[:0], w, wl.eps, out[:0], rout[:0], stream)
+    info = tw.load_library().tw_fused_launch_info
+    info_args = (parts.shape[0], 64, wl.hidden, 1 if wl.dtype == "bf16" else 0, stream.cuda_stream,
+                 tw._lib.LaunchInfo())
     cache = tw.SplitPlanCache(**plan_kw)
     calls = {
         "eager_stacked": lambda: tw.tw_fused_reduce_rmsnorm(p64, r64, w, wl.eps, out=o64,
@@ -243,6 +250,8 @@ def run_host_cost(tw, torch, wl, sets, w, stream, plan_kw) -> dict:
         "eager_shard": lambda: tw.tw_shard_rmsnorm(p64, r64, w, wl.eps, 0, out=o64,
                                                    residual_out=ro64),
         "prepared": prepared,
+        "prepared_zero_rows": prepared_empty,
+        "launch_info_c": lambda: info(*info_args),
         "split_plan_cached": lambda: cache(wl.num_tokens),
         "split_plan_c": lambda: tw.tw_split_plan(wl.num_tokens, **plan_kw),
     }

@@ -230,11 +230,19 @@ class _on_device:
             self._ctx.__exit__(*exc)
 
 
+# torch's current stream of a device as its raw hipStream_t, without making a
+# Stream object (a per-call cost); the public call where torch lacks it.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_handle(device: torch.device, stream: Optional[torch.cuda.Stream]):
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    if s.device != device:
-        raise ValueError(f"the stream belongs to {s.device}, the tensors to {device}")
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is None:
+        if _raw_stream is not None:
+            return _raw_stream(device.index)
+        stream = torch.cuda.current_stream(device)
+    if stream.device != device:
+        raise ValueError(f"the stream belongs to {stream.device}, the tensors to {device}")
+    return stream.cuda_stream
 
 
 def tw_fused_reduce_rmsnorm(partials, residual: torch.Tensor, weight: torch.Tensor, eps: float,
