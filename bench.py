@@ -295,6 +295,20 @@ def run_launch_floor(torch, timer) -> dict:
         print(f"[bench] empty kernel, {grid} workgroups of 1024 threads: {us:.2f} us per launch "
               f"(graph replay)", file=sys.stderr, flush=True)
         del g
+    # Host time of one launch through each launch API (a C++ loop in the probe
+    # library, so that Python does not bound it).
+    host = {}
+    out = ctypes.c_double()
+    for api, name in ((0, "hipLaunchKernel"), (1, "hipModuleLaunchKernel"),
+                      (2, "hipExtLaunchKernel")):
+        for grid in (64, 1024):
+            rc = lib.tw_probe_launch_cost(api, grid, 2000, cap.cuda_stream, ctypes.byref(out))
+            if rc != 0:
+                raise RuntimeError(f"launch cost probe failed: {rc}")
+            host[f"{name}_{grid}"] = round(out.value, 3)
+            print(f"[bench] host time per {name} of {grid} empty workgroups: {out.value:.2f} us",
+                  file=sys.stderr, flush=True)
+    res["host_us_per_launch"] = host
     return res
 
 
@@ -495,6 +509,9 @@ def _probe_lib():
                                          ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
                                          ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     lib.tw_probe_twin_launch.restype = ctypes.c_int
+    lib.tw_probe_launch_cost.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.POINTER(ctypes.c_double)]
+    lib.tw_probe_launch_cost.restype = ctypes.c_int
     return lib
 
 

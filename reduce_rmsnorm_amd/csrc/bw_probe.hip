@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 
 #include <array>
+#include <chrono>
 #include <cstdint>
 #include <utility>
 
@@ -253,6 +254,50 @@ extern "C" int tw_probe_twin_launch(int kind, int sequenced, const void* const* 
   const int block = c == 1 ? 512 : 1024;
   return (int)hipLaunchKernel((const void*)fn, dim3(grid), dim3(block), args, 0,
                               static_cast<hipStream_t>(stream));
+}
+
+// Host time of one launch of the empty kernel through a launch API: api 0
+// hipLaunchKernel, 1 hipModuleLaunchKernel on a function handle fetched once,
+// 2 hipExtLaunchKernel.  `launches` back-to-back launches of `grid`
+// workgroups on `stream`, timed on the host with no synchronization inside the
+// loop, best of five; *us_per_launch receives the time per launch.  The caller
+// keeps `launches` small enough for the GPU to keep up (an empty launch takes
+// under 2 us).  Returns 0 or a HIP error code; -1 for arguments out of range.
+extern "C" int tw_probe_launch_cost(int api, int grid, int launches, void* stream,
+                                    double* us_per_launch) {
+  if (api < 0 || api > 2 || grid < 1 || grid > 65536 || launches < 1 || launches > 100000 ||
+      us_per_launch == nullptr)
+    return -1;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  ProbeArgs e{};
+  void* args[] = {&e};
+  hipFunction_t f = nullptr;
+  if (api == 1) {
+    const hipError_t r = hipGetFuncBySymbol(&f, (const void*)&probe_empty);
+    if (r != hipSuccess) return (int)r;
+  }
+  auto one = [&]() -> hipError_t {
+    if (api == 0)
+      return hipLaunchKernel((const void*)&probe_empty, dim3(grid), dim3(kEmptyBlock), args, 0, s);
+    if (api == 1) return hipModuleLaunchKernel(f, grid, 1, 1, kEmptyBlock, 1, 1, 0, s, args, nullptr);
+    return hipExtLaunchKernel((const void*)&probe_empty, dim3(grid), dim3(kEmptyBlock), args, 0, s,
+                              nullptr, nullptr, 0);
+  };
+  double best = 1e30;
+  for (int rep = 0; rep < 6; ++rep) {
+    hipError_t r = hipStreamSynchronize(s);
+    if (r != hipSuccess) return (int)r;
+    const auto t0 = std::chrono::steady_clock::now();
+    for (int i = 0; i < launches; ++i)
+      if ((r = one()) != hipSuccess) return (int)r;
+    const auto t1 = std::chrono::steady_clock::now();
+    const double us = std::chrono::duration<double, std::micro>(t1 - t0).count() / launches;
+    if (rep > 0 && us < best) best = us;     // the first pass warms up
+  }
+  const hipError_t r = hipStreamSynchronize(s);
+  if (r != hipSuccess) return (int)r;
+  *us_per_launch = best;
+  return 0;
 }
 
 extern "C" int tw_probe_launch(int kind, const void* const* src, int nsrc, void* const* dst,
