@@ -369,14 +369,16 @@ void fused_reduce_rmsnorm_strided_kernel(const u32x4* k_first, int64_t k_row_beg
 // sketch partitions tokens over its CTAs (tokens per CTA = ceil(T / grid)).
 // A barrier between rows keeps a row's wave partial sums from overwriting the
 // previous row's while a slower wave still reads them.  Few workgroups are
-// launched by design, so no occupancy cap is requested.
-template <int N, int BLOCK, int VPT, bool BF16, int CHUNK, int SEQ, int PACE>
+// launched by design, so no occupancy cap is requested.  WT picks the store
+// form by the grid (rows_form below): with fewer workgroups than CUs the plain
+// non-temporal stores are the faster, from one workgroup per CU on the
+// write-through ones (profiles: "Store form of the consecutive-rows kernel").
+template <int N, int BLOCK, int VPT, bool BF16, int CHUNK, int SEQ, int PACE, bool WT>
 __global__ __launch_bounds__(BLOCK) void fused_reduce_rmsnorm_rows_kernel(KArgs a,
                                                                           int64_t rows_per_wg,
                                                                           int64_t row_end) {
   constexpr int E = Elem<BF16>::kPerVec;
   constexpr int NW = BLOCK / 64;
-  constexpr bool WT = true;
   __shared__ float wave_part[NW];
   const u32x4* const k_first = a.partials[0];
   const int32_t k_nvec = a.nvec;
@@ -455,13 +457,21 @@ constexpr std::array<std::array<KernelFn, kMaxPartials>, sizeof...(Gs)> both_slo
     std::integer_sequence<int, Gs...>) {
   return {both_slots_row_of<BF16, Gs>(std::make_integer_sequence<int, kMaxPartials>{})...};
 }
-template <bool BF16, bool SEQ_ORDER, int G, int... Ns>
+// Forms of the consecutive-rows kernel, picked by the launched grid:
+//   0  fewer workgroups than CUs: all loads at once, plain non-temporal stores;
+//   1  a workgroup on every CU, less than a round: all at once, write-through;
+//   2  a round or more: the sequenced order, write-through.
+constexpr int kRowsForms = 3;
+constexpr int rows_form(int64_t grid, int64_t round, int num_cus) {
+  return grid >= round ? 2 : grid >= num_cus ? 1 : 0;
+}
+template <bool BF16, int FORM, int G, int... Ns>
 constexpr std::array<RowsKernelFn, sizeof...(Ns)> rows_row_of(std::integer_sequence<int, Ns...>) {
   return {&fused_reduce_rmsnorm_rows_kernel<Ns + 1, fused_geometry(G, Ns + 1).block,
                                             fused_geometry(G, Ns + 1).vpt, BF16,
                                             fused_geometry(G, Ns + 1).chunk,
-                                            load_order(G, Ns + 1, SEQ_ORDER),
-                                            load_pace(G, Ns + 1, SEQ_ORDER)>...};
+                                            load_order(G, Ns + 1, FORM == 2),
+                                            load_pace(G, Ns + 1, FORM == 2), FORM != 0>...};
 }
 
 template <bool BF16, bool SEQ_ORDER, int... Gs>
@@ -469,10 +479,10 @@ constexpr std::array<std::array<KernelFn, kMaxPartials>, sizeof...(Gs)> table_of
     std::integer_sequence<int, Gs...>) {
   return {row_of<BF16, SEQ_ORDER, Gs>(std::make_integer_sequence<int, kMaxPartials>{})...};
 }
-template <bool BF16, bool SEQ_ORDER, int... Gs>
+template <bool BF16, int FORM, int... Gs>
 constexpr std::array<std::array<RowsKernelFn, kMaxPartials>, sizeof...(Gs)> rows_table_of(
     std::integer_sequence<int, Gs...>) {
-  return {rows_row_of<BF16, SEQ_ORDER, Gs>(std::make_integer_sequence<int, kMaxPartials>{})...};
+  return {rows_row_of<BF16, FORM, Gs>(std::make_integer_sequence<int, kMaxPartials>{})...};
 }
 
 using Geoms = std::make_integer_sequence<int, kNumGeometries>;
@@ -486,9 +496,13 @@ const std::array<std::array<std::array<KernelFn, kMaxPartials>, kNumGeometries>,
 // [bf16]
 const std::array<std::array<std::array<KernelFn, kMaxPartials>, kNumGeometries>, 2> kBothSlotsTable = {
     {both_slots_table_of<false>(Geoms{}), both_slots_table_of<true>(Geoms{})}};
-const std::array<std::array<std::array<std::array<RowsKernelFn, kMaxPartials>, kNumGeometries>, 2>, 2>
-    kRowsTable = {{{rows_table_of<false, false>(Geoms{}), rows_table_of<false, true>(Geoms{})},
-                   {rows_table_of<true, false>(Geoms{}), rows_table_of<true, true>(Geoms{})}}};
+// [bf16][rows_form]
+const std::array<
+    std::array<std::array<std::array<RowsKernelFn, kMaxPartials>, kNumGeometries>, kRowsForms>, 2>
+    kRowsTable = {{{rows_table_of<false, 0>(Geoms{}), rows_table_of<false, 1>(Geoms{}),
+                    rows_table_of<false, 2>(Geoms{})},
+                   {rows_table_of<true, 0>(Geoms{}), rows_table_of<true, 1>(Geoms{}),
+                    rows_table_of<true, 2>(Geoms{})}}};
 
 }  // namespace
 
@@ -555,10 +569,11 @@ int launch_fused(const FusedLaunch& L, char* err, size_t errlen) {
   } else {
     const int64_t cap = max_rows_per_dispatch(block);
     const int64_t wgs = L.max_workgroups < cap ? L.max_workgroups : cap;
-    const RowsKernelFn fn = kRowsTable[bf16][wgs >= round_rows(block, L.num_cus)][g][L.num_partials - 1];
     int64_t rows_per_wg = (L.num_rows + wgs - 1) / wgs;
     int64_t row_end = L.row_begin + L.num_rows;
     const unsigned grid = (unsigned)((L.num_rows + rows_per_wg - 1) / rows_per_wg);
+    const int form = rows_form(grid, round_rows(block, L.num_cus), L.num_cus);
+    const RowsKernelFn fn = kRowsTable[bf16][form][g][L.num_partials - 1];
     void* args[] = {&k, &rows_per_wg, &row_end};
     e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(block), args, 0,
                         static_cast<hipStream_t>(L.stream));

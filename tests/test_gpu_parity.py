@@ -254,13 +254,17 @@ def test_unfused_comparator_matches_its_oracle(name, T, h):
 
 # --------------------------------------------- fixed number of workgroups ----
 
-@pytest.mark.parametrize("name,T,h", [("llama70b", 1024, 8192), ("tiny", 64, 512), ("mixtral", 333, 4096)])
+# The grid picks the consecutive-rows kernel's form: fewer workgroups than CUs,
+# at least one per CU, or a whole round (2500 rows at G = 1251 launch 1250
+# workgroups of two rows, more than a round of 512-thread workgroups).
+@pytest.mark.parametrize("name,T,h", [("llama70b", 1024, 8192), ("tiny", 64, 512), ("mixtral", 333, 4096),
+                                      ("mixtral", 2500, 4096)])
 def test_grid_launch_bit_identical_to_one_row_per_workgroup(name, T, h):
     d = make_inputs(name, num_tokens=T, hidden=h)
     parts, res, w = upload(d)
     say(f"grid reference {name}: T={T} h={h}")
     out_ref, rout_ref = _run_full(parts, res, w, d["eps"])
-    for G in (1, 2, 3, 8, 100, 256, T - 1, T, T + 5):
+    for G in (1, 2, 3, 8, 100, 256, T // 2 + 1, T - 1, T, T + 5):
         if G < 1:
             continue
         say(f"grid {name}: {G} workgroups")
