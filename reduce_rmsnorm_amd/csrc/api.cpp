@@ -149,14 +149,14 @@ tw_status check_scalars(int32_t n, int64_t T, int64_t h, float eps, tw_dtype dty
     return TW_ERR_INVALID_ARG;
   }
   const int64_t es = dtype == TW_BF16 ? 2 : 4;
+  if (h > TW_MAX_ROW_BYTES / es) {             // before any product with h
+    set_error("%s: hidden=%lld exceeds %lld elements", who, (long long)h,
+              (long long)(TW_MAX_ROW_BYTES / es));
+    return TW_ERR_UNSUPPORTED;
+  }
   if ((h * es) % 16 != 0) {
     set_error("%s: hidden=%lld is not a multiple of %lld elements (16 bytes)", who,
               (long long)h, (long long)(16 / es));
-    return TW_ERR_UNSUPPORTED;
-  }
-  if (h * es > TW_MAX_ROW_BYTES) {
-    set_error("%s: hidden=%lld exceeds %lld elements", who, (long long)h,
-              (long long)(TW_MAX_ROW_BYTES / es));
     return TW_ERR_UNSUPPORTED;
   }
   if (T > TW_MAX_TOKENS) {

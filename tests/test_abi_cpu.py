@@ -83,6 +83,8 @@ def _call(lib, n=2, T=4, h=64, eps=1e-5, dtype=1, parts=None, res=A + 10 * MB, w
     (dict(h=6, dtype=0), UNSUPPORTED, "multiple"),      # fp32 needs h % 4 == 0
     (dict(h=65544), UNSUPPORTED, "exceeds"),
     (dict(h=32772, dtype=0), UNSUPPORTED, "exceeds"),
+    (dict(h=2 ** 62 + 4), UNSUPPORTED, "exceeds"),      # h * 2 would overflow int64
+    (dict(h=2 ** 63 - 1, dtype=0), UNSUPPORTED, "exceeds"),
     (dict(T=2 ** 31), UNSUPPORTED, "exceeds"),
     (dict(parts=False), INVALID, "partials array is NULL"),
     (dict(parts=[A, 0]), INVALID, "partials[1] is NULL"),
