@@ -18,9 +18,9 @@
 // The schedule twins bound the fused kernel's own schedule rather than a flat
 // stream: one workgroup per row of the fused kernel's geometry (geometry.h),
 // its load order (the N+1 tensors in summation order, one in flight per
-// thread, with the same pause between tensors, or all at once), its
-// non-temporal stores of both outputs and its one LDS barrier per row, with
-// the arithmetic replaced by an xor.  What a twin gains over the fused kernel
+// thread, with the same pause between tensors, or all at once), its stores of
+// both outputs (the same write-through streaming buffer stores) and its one
+// LDS barrier per row, with the arithmetic replaced by an xor.  What a twin gains over the fused kernel
 // is what the arithmetic costs; what it lacks against the peak is the
 // schedule's own bound.
 
@@ -31,6 +31,7 @@
 #include <cstdint>
 #include <utility>
 
+#include "device_common.h"
 #include "geometry.h"
 
 namespace {
@@ -121,8 +122,8 @@ __global__ __launch_bounds__(kPlacementBlock) void probe_placement(ProbeArgs a) 
 // taken one at a time, and each slot's tensors are loaded in order with one
 // in flight (SEQ) and a pause of PACE * 64 clocks after each, or all at once
 // (!SEQ).  WRITES: both outputs are stored (residual_out per slot, out after
-// the barrier); otherwise the loads are kept alive by a store that never
-// happens for real data.
+// the barrier) with the fused kernel's store (store_stream); otherwise the
+// loads are kept alive by a store that never happens for real data.
 template <int NSRC, int BLOCK, int VPT, bool SEQ, int PACE, bool WRITES>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8)))
 void probe_row_twin(ProbeArgs a) {
@@ -152,7 +153,8 @@ void probe_row_twin(ProbeArgs a) {
 #pragma unroll
       for (int i = 1; i < NSRC; ++i) acc[j] ^= raw[i];
     }
-    if constexpr (WRITES) __builtin_nontemporal_store(acc[j], a.dst[1] + v);
+    if constexpr (WRITES)
+      tw::dev::store_stream(acc[j], a.dst[1] + base, tid + j * BLOCK, BLOCK * VPT * 16);
   }
   unsigned x = 0;
 #pragma unroll
@@ -166,7 +168,7 @@ void probe_row_twin(ProbeArgs a) {
   for (int j = 0; j < VPT; ++j) {
     const int64_t v = base + tid + j * BLOCK;
     const u32x4 o = acc[j] + tot;
-    if constexpr (WRITES) __builtin_nontemporal_store(o, a.dst[0] + v);
+    if constexpr (WRITES) tw::dev::store_stream(o, a.dst[0] + base, tid + j * BLOCK, BLOCK * VPT * 16);
     else if (o.x == 0x7F7F1234u && o.y == 0x00001234u && o.z == 0x5A5A5A5Au) a.dst[0][v] = o;
   }
 }
