@@ -25,14 +25,14 @@ inline int64_t max_rows_per_dispatch(int block) { return kMaxLaunchWorkItems / b
 // streams: single launches lose speed beyond about 768 MiB, in proportion to
 // the bytes rather than the rows (profiles/launch_rules_mi355x.md, "Dispatch
 // size").  Longer launches are therefore cut into dispatches over consecutive
-// row ranges of about equal size, none above this many bytes and each at
-// least one round of resident workgroups.
+// row ranges of about equal size, none above this many bytes unless one round
+// of resident workgroups alone streams more.
 constexpr int64_t kMaxDispatchBytes = int64_t(768) << 20;
 
-// Rows per dispatch for rows of row_bytes (all tensors of a row, read and
-// written) when round_rows workgroups are resident at once: a whole number of
-// rounds within kMaxDispatchBytes (at least one round), and never above the
-// work-item limit.
+// The most rows one dispatch takes, for rows of row_bytes (all tensors of a
+// row, read and written) when round_rows workgroups are resident at once: a
+// whole number of rounds within kMaxDispatchBytes (at least one round), and
+// never above the work-item limit.
 inline int64_t fused_rows_per_dispatch(int block, int64_t row_bytes, int64_t round_rows) {
   int64_t cap = kMaxDispatchBytes / row_bytes;
   cap -= cap % round_rows;
