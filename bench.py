@@ -7,12 +7,13 @@ kernel launch(es) it calls for.  At the default workload (Llama-3-70B-shaped:
 T=1024 tokens, h=8192, N=8 bf16 partials) the planner keeps the batch whole
 (its GEMM is one wave on 256 CUs), so a step is one fused launch.
 
-Timing: W untimed warm-up steps, then K timed steps back to back on the
-current torch stream -- the stream the library enqueues on -- between two HIP
-events, with torch.cuda.synchronize() on both sides.  By default W is as many
-steps as take about 100 ms: from a pause the GPU needs about 30 ms of load to
-reach its steady speed.  The host launches every step; with --graph the same
-launches are recorded into HIP graphs and the timed steps are graph replays.
+Timing: a settle of as many steps as take about 100 ms (from a pause the GPU
+needs about 30 ms of load to reach its steady speed; it always runs and is
+reported as `settle`), then W untimed warm-up steps, then K timed steps back
+to back on the current torch stream -- the stream the library enqueues on --
+between two HIP events, with torch.cuda.synchronize() on both sides.  The
+host launches every step; with --graph the same launches are recorded into
+HIP graphs and the timed steps are graph replays.
 Whole buffer sets (inputs and outputs) rotate so that the inputs, and the
 outputs on their own, touched between two uses of one set each exceed twice
 the 256 MB last-level (MALL) cache: reads are served by HBM, and no output
