@@ -94,7 +94,8 @@ struct KArgs {
 // Store of an output vector VEC of the row at `base`: written through the L2
 // (store_stream) where the kernel's constant WT says so, else a plain
 // non-temporal store (the strided kernel's many-partial forms, where the
-// buffer store's offset register would spill at the occupancy cap).
+// buffer store's offset register would spill at the occupancy cap, and the
+// consecutive-rows kernel on fewer workgroups than CUs).
 #define TW_STORE(V, TENSOR, VEC)                                                       \
   {                                                                                    \
     if constexpr (WT) store_stream((V), (TENSOR) + base, (VEC), nvec * 16);           \
